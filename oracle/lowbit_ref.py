@@ -1,0 +1,191 @@
+"""Plain numpy/fp64 reference for the packed low-bit weight GEMM (test infrastructure only).
+
+What is computed (model-card and guide passages cited per function):
+
+    Y[m, n] = sum_k  X[m, k] * c[n, k] * S[n, k // g]
+
+with X given as bf16 bit patterns, c the integer weight codes (ternary {-1, 0, +1} or
+binary {-1, +1}), S the fp16 group scales, all evaluated in fp64.  Every product
+bf16 * fp16 * {-1, 0, 1} has at most 8 + 11 significant bits and is exact in fp64, so
+this is the exact result up to the summation order of the fp64 matmul.
+
+Readings taken where the pages are silent (each also recorded with the format
+definition in include/lowbit.h):
+
+R1  Ternary encoding: 2-bit field 00 -> 0, 01 -> +1, 10 -> -1.  The field 11 never comes
+    out of the packer; the unpacker maps it to 0 via c = (f & 1) - ((f >> 1) & 1).
+R2  Word order: 16 ternary (32 binary) codes per uint32, consecutive along K, least
+    significant field first: code k lives in word k // 16 at bits 2*(k % 16) .. +1
+    (binary: word k // 32, bit k % 32, bit 1 -> +1, bit 0 -> -1).
+R3  Layout: packed words [N, K*bits/32] and scales [N, K/g], both row-major by output
+    feature n.
+R4  Scale form: symmetric w = s * c for ternary too (the binary model card gives
+    w = scale_g * b; no zero point is mentioned anywhere).
+R5  Invalid codes handed to the packer (ternary outside {-1,0,1}, binary outside
+    {-1,1}) are packed as 0 bits and counted.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Tuple
+
+import numpy as np
+
+TERNARY = 2
+BINARY = 1
+
+REL_FROB_TOL = 5e-3
+ELEM_TOL = 1e-2
+
+
+# ----------------------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64.  A bf16 number is the upper half of an IEEE binary32,
+    so widening is exact."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits_rne(y: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bf16 (8 significant bits, 8 exponent bits), ties to even.
+
+    Written from the definition: split |y| = f * 2**e with f in [0.5, 1), keep 8
+    significant bits by rounding |y| / 2**(e-8) to the nearest integer (numpy's rint
+    rounds halves to even), with the quantum floored at bf16's subnormal spacing 2**-133;
+    overflow goes to infinity.  The rounded value is representable in binary32, whose
+    upper 16 bits are the bf16 pattern."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros(y.shape, dtype=np.uint16)
+    a = np.abs(y)
+    nz = a > 0
+    f, e = np.frexp(a[nz])
+    quantum_exp = np.maximum(e - 8, -133)
+    q = np.rint(np.ldexp(a[nz], -quantum_exp))
+    val = np.ldexp(q, quantum_exp)
+    with np.errstate(over="ignore"):
+        v32 = val.astype(np.float32)
+    bits = (v32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits[val >= 2.0 ** 128] = 0x7F80
+    out[nz] = bits
+    out |= np.where(np.signbit(y), np.uint16(0x8000), np.uint16(0))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Packing (readings R1, R2, R5)
+# ----------------------------------------------------------------------------------------
+
+def pack(codes: np.ndarray, bits: int) -> Tuple[np.ndarray, int]:
+    """int8 codes [N, K] -> (uint32 words [N, K*bits/32], number of invalid codes).
+
+    Ternary: field(c) = 01 for +1, 10 for -1, 00 for 0, placed at bits 2*(k % 16) of word
+    k // 16.  Binary: bit 1 for +1, bit 0 for -1, at bit k % 32 of word k // 32."""
+    c = np.asarray(codes, dtype=np.int8)
+    if c.ndim != 2:
+        raise ValueError("codes must be 2-D [N, K]")
+    N, K = c.shape
+    per_word = 32 // bits
+    if bits not in (TERNARY, BINARY) or K % per_word:
+        raise ValueError("bits must be 1 or 2 and K a multiple of 32/bits")
+    field = np.zeros((N, K), dtype=np.uint32)
+    if bits == TERNARY:
+        field[c == 1] = 1
+        field[c == -1] = 2
+        bad = int(np.count_nonzero((c != 0) & (c != 1) & (c != -1)))
+    else:
+        field[c == 1] = 1
+        bad = int(np.count_nonzero((c != 1) & (c != -1)))
+    field = field.reshape(N, K // per_word, per_word)
+    words = np.zeros((N, K // per_word), dtype=np.uint32)
+    for i in range(per_word):
+        words |= field[:, :, i] << np.uint32(bits * i)
+    return words, bad
+
+
+def unpack(words: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """uint32 words [N, K*bits/32] -> int8 codes [N, K].
+
+    Ternary: c = (f & 1) - ((f >> 1) & 1) for each 2-bit field f (so 11 decodes to 0).
+    Binary: c = 2 * bit - 1."""
+    w = np.asarray(words, dtype=np.uint32)
+    per_word = 32 // bits
+    N = w.shape[0]
+    if w.shape[1] * per_word != K:
+        raise ValueError("words do not hold K codes per row")
+    out = np.zeros((N, w.shape[1], per_word), dtype=np.int8)
+    for i in range(per_word):
+        f = (w >> np.uint32(bits * i)) & np.uint32((1 << bits) - 1)
+        if bits == TERNARY:
+            out[:, :, i] = (f & 1).astype(np.int8) - ((f >> 1) & 1).astype(np.int8)
+        else:
+            out[:, :, i] = 2 * f.astype(np.int8) - 1
+    return out.reshape(N, K)
+
+
+# ----------------------------------------------------------------------------------------
+# Dequantise and matmul
+# ----------------------------------------------------------------------------------------
+
+def dequant_f64(codes: np.ndarray, scales: np.ndarray, g: int) -> np.ndarray:
+    """W[n, k] = c[n, k] * S[n, k // g] in fp64 (exact).
+
+    The model card's binary form w_i = scale_g * b_i with one fp16 scale per group of g
+    consecutive weights along the input dimension; ternary takes the same symmetric
+    form (reading R4)."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    N, K = c.shape
+    if K % g or s.shape != (N, K // g):
+        raise ValueError("scales must be [N, K // g]")
+    s_per_k = np.repeat(s, g, axis=1)  # S[n, k // g] for every k
+    return c * s_per_k
+
+
+def gemm_ref_f64(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, g: int) -> np.ndarray:
+    """Y = X @ dequant(W).T in fp64: dequantise to dense, then an ordinary matmul (the
+    shape of the CPU bring-up path in the Bonsai-Image-Demo report)."""
+    xd = bf16_bits_to_f64(x_bits)
+    wd = dequant_f64(codes, scales, g)
+    if xd.shape[1] != wd.shape[1]:
+        raise ValueError("X and W disagree on K")
+    return xd @ wd.T
+
+
+def gemm_ref_from_words(x_bits: np.ndarray, words: np.ndarray, scales: np.ndarray,
+                        K: int, g: int, bits: int) -> np.ndarray:
+    """The same reference starting from packed words (unpack, dequantise, matmul)."""
+    return gemm_ref_f64(x_bits, unpack(words, K, bits), scales, g)
+
+
+def gemm_fsum_element(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, g: int,
+                      m: int, n: int) -> float:
+    """One output element as the correctly rounded sum (math.fsum) of its exact products."""
+    x = bf16_bits_to_f64(np.asarray(x_bits)[m])
+    c = np.asarray(codes)[n]
+    s = np.asarray(scales, dtype=np.float16)[n].astype(np.float64)
+    return math.fsum(float(x[k]) * int(c[k]) * float(s[k // g]) for k in range(c.shape[0]))
+
+
+# ----------------------------------------------------------------------------------------
+# Acceptance
+# ----------------------------------------------------------------------------------------
+
+def check_tolerance(y: np.ndarray, yref: np.ndarray, rel_frob_tol: float = REL_FROB_TOL,
+                    elem_tol: float = ELEM_TOL) -> Dict[str, float]:
+    """Accept y iff ||y - yref||_F / ||yref||_F <= rel_frob_tol and, for every element,
+    |y - yref| <= elem_tol * (|yref| + 1).  `y` may be bf16 bit patterns (uint16) or
+    floats."""
+    y = np.asarray(y)
+    yf = bf16_bits_to_f64(y) if y.dtype == np.uint16 else y.astype(np.float64)
+    yref = np.asarray(yref, dtype=np.float64)
+    err = yf - yref
+    nref = float(np.linalg.norm(yref))
+    rel = float(np.linalg.norm(err)) / nref if nref > 0 else float(np.linalg.norm(err))
+    ratio = np.abs(err) / (np.abs(yref) + 1.0)
+    max_ratio = float(ratio.max()) if ratio.size else 0.0
+    finite = bool(np.all(np.isfinite(yf)))
+    ok = finite and rel <= rel_frob_tol and max_ratio <= elem_tol
+    return {"ok": ok, "rel_frob": rel, "max_ratio": max_ratio, "finite": finite}

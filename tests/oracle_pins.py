@@ -1,0 +1,193 @@
+"""Pins that tie the oracle to facts outside itself.
+
+Each pin takes the oracle as an object `o` exposing pack / unpack / dequant_f64 /
+gemm_ref_f64 / gemm_fsum_element, so that tests/test_oracle.py can run every pin on the
+real oracle (all must pass) and on copies with a planted mistake (some pin must fail).
+None of these re-types the oracle's formulas: the expected values come from hand-worked
+golden words, bit strings built a different way, math.fsum of exact products,
+closed-form statistics, exact algebraic identities, or a library matmul.
+"""
+from __future__ import annotations
+
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+from workloads import gen_codes, gen_scales, gen_x, rng_for
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pack_words.txt")
+
+
+def load_golden():
+    rows = []
+    with open(GOLDEN) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            b, name, codes, word = [s.strip() for s in line.split("|")]
+            rows.append((int(b), name, np.array([int(v) for v in codes.split(",")], dtype=np.int8),
+                         int(word, 16)))
+    return rows
+
+
+def real_oracle():
+    import oracle
+    return SimpleNamespace(pack=oracle.pack, unpack=oracle.unpack, dequant_f64=oracle.dequant_f64,
+                           gemm_ref_f64=oracle.gemm_ref_f64, gemm_fsum_element=oracle.gemm_fsum_element,
+                           bf16_bits_to_f64=oracle.bf16_bits_to_f64)
+
+
+# ----------------------------------------------------------------------------------------
+
+def pin_golden_words(o):
+    """Packing and unpacking reproduce the hand-worked golden words."""
+    for bits, name, codes, word in load_golden():
+        w, bad = o.pack(codes[None, :], bits)
+        assert bad == 0, name
+        assert w.shape == (1, 1) and int(w[0, 0]) == word, f"{name}: {int(w[0, 0]):#010x} != {word:#010x}"
+        back = o.unpack(np.array([[word]], dtype=np.uint32), codes.size, bits)
+        assert np.array_equal(back[0], codes), name
+
+
+def pin_bitstring(o, seed=11):
+    """Words equal integers parsed from bit strings written most-significant field first."""
+    rng = np.random.default_rng(seed)
+    for bits in (2, 1):
+        per = 32 // bits
+        codes = gen_codes(rng, 5, 4 * per, bits)
+        w, _ = o.pack(codes, bits)
+        for n in range(codes.shape[0]):
+            for j in range(4):
+                chunk = codes[n, j * per:(j + 1) * per]
+                if bits == 2:
+                    fields = ["01" if c == 1 else "10" if c == -1 else "00" for c in chunk]
+                else:
+                    fields = ["1" if c == 1 else "0" for c in chunk]
+                expect = int("".join(reversed(fields)), 2)
+                assert int(w[n, j]) == expect
+
+
+def pin_group_blocks(o):
+    """Scale group membership: with X = 1 on exactly one run of g consecutive k and all
+    codes +1, Y[m, n] = g * (scale of that run).  The expected value picks the scale by
+    the run's position, not by evaluating k // g."""
+    K, g, N = 256, 64, 3
+    scales = (np.arange(N * (K // g)).reshape(N, K // g) + 1).astype(np.float16) / np.float16(16)
+    codes = np.ones((N, K), dtype=np.int8)
+    for run in range(K // g):
+        x = np.zeros((1, K), dtype=np.uint16)
+        x[0, run * g:(run + 1) * g] = 0x3F80  # bf16 1.0
+        y = o.gemm_ref_f64(x, codes, scales, g)
+        for n in range(N):
+            assert y[0, n] == g * float(scales[n, run]), (run, n)
+
+
+def pin_one_hot(o):
+    """Exactly one nonzero code c[n0, k0] = -1: Y[:, n0] = -S[n0, grp] * X[:, k0] where grp is
+    the run of g consecutive k holding k0 (worked out by hand below), and every other
+    column is exactly 0.  The square case catches a transposed decode."""
+    rng = rng_for(5, 99, 0)
+    for (M, N, K, g, cases) in ((4, 8, 128, 32, ((0, 0, 0), (3, 31, 0), (5, 32, 1), (7, 127, 3), (2, 77, 2))),
+                                (3, 64, 64, 32, ((1, 40, 1), (50, 3, 0)))):
+        x = gen_x(rng, M, K)
+        s = gen_scales(rng, N, K, g)
+        xf = o.bf16_bits_to_f64(x)
+        for (n0, k0, grp) in cases:
+            c = np.zeros((N, K), dtype=np.int8)
+            c[n0, k0] = -1
+            w, _ = o.pack(c, 2)
+            y = o.gemm_ref_f64(x, o.unpack(w, K, 2), s, g)
+            assert np.array_equal(y[:, n0], -float(s[n0, grp]) * xf[:, k0]), (n0, k0)
+            assert not np.any(np.delete(y, n0, axis=1)), (n0, k0)
+
+
+def pin_unpack_unused_field(o):
+    """The ternary field 11 (never written by the packer) decodes to 0; a binary word of
+    all ones decodes to all +1."""
+    w = np.full((2, 3), 0xFFFFFFFF, dtype=np.uint32)
+    assert not np.any(o.unpack(w, 48, 2))
+    assert np.all(o.unpack(w, 96, 1) == 1)
+
+
+def pin_fsum(o, M=64, N=256, K=256, g=64, bits=2, seed=0):
+    """fp64 dgemm result within a few ulps of the correctly rounded exact sum."""
+    x = gen_x(rng_for(seed, 0, 0), M, K)
+    c = gen_codes(rng_for(seed, 0, 1), N, K, bits)
+    s = gen_scales(rng_for(seed, 0, 2), N, K, g)
+    y = o.gemm_ref_f64(x, c, s, g)
+    xf = o.bf16_bits_to_f64(x)
+    sf = np.repeat(s.astype(np.float64), g, axis=1)
+    for m in range(M):
+        for n in range(N):
+            terms = [float(a) * int(b) * float(t) for a, b, t in zip(xf[m], c[n], sf[n])]
+            exact = math.fsum(terms)
+            bound = 4 * K * np.finfo(np.float64).eps * math.fsum(abs(t) for t in terms)
+            assert abs(y[m, n] - exact) <= bound, (m, n, y[m, n], exact)
+    # and the single-element brute force agrees bit for bit with the fsum above
+    for (m, n) in ((0, 0), (M - 1, N - 1), (M // 3, N // 2 + 1)):
+        e = o.gemm_fsum_element(x, c, s, g, m, n)
+        terms = [float(a) * int(b) * float(t) for a, b, t in zip(xf[m], c[n], sf[n])]
+        assert e == math.fsum(terms)
+
+
+def pin_statistics(o, bits=2, M=128, N=256, K=3072, g=64, seed=3):
+    """E[y] = 0 and Var(y) = K * P(c != 0) * E[s^2] * E[x^2] for independent inputs with
+    x ~ N(0,1), s ~ U[0.005, 0.05] (E[s^2] = (a^2 + ab + b^2)/3 = 9.25e-4)."""
+    x = gen_x(rng_for(seed, 7, 0), M, K)
+    c = gen_codes(rng_for(seed, 7, 1), N, K, bits)
+    s = gen_scales(rng_for(seed, 7, 2), N, K, g)
+    y = o.gemm_ref_f64(x, c, s, g)
+    p_nz = 0.5 if bits == 2 else 1.0
+    var = K * p_nz * (0.005 ** 2 + 0.005 * 0.05 + 0.05 ** 2) / 3.0
+    assert abs(y.mean()) < 0.05 * math.sqrt(var)
+    assert abs(y.var() / var - 1.0) < 0.06, (y.var(), var)
+
+
+def pin_linearity(o, seed=4):
+    """Exact identities: Y(2^e S) = 2^e Y(S), Y(-X) = -Y(X), Y(-c) = -Y(c)."""
+    M, N, K, g = 16, 32, 256, 64
+    x = gen_x(rng_for(seed, 8, 0), M, K)
+    c = gen_codes(rng_for(seed, 8, 1), N, K, 2)
+    s = gen_scales(rng_for(seed, 8, 2), N, K, g)
+    y = o.gemm_ref_f64(x, c, s, g)
+    y2 = o.gemm_ref_f64(x, c, (s.astype(np.float32) * 4).astype(np.float16), g)
+    assert np.array_equal(y2, 4 * y)
+    assert np.array_equal(o.gemm_ref_f64(x ^ np.uint16(0x8000), c, s, g), -y)
+    assert np.array_equal(o.gemm_ref_f64(x, -c, s, g), -y)
+    zero = o.gemm_ref_f64(x, np.zeros_like(c), s, g)
+    assert not np.any(zero)
+
+
+def pin_library_matmul(o, seed=6):
+    """With every scale 1, dequant(W) is the codes themselves and Y is a plain matmul,
+    here computed by torch's CPU matmul in float64."""
+    import torch
+    M, N, K, g = 32, 48, 192, 64
+    x = gen_x(rng_for(seed, 9, 0), M, K)
+    c = gen_codes(rng_for(seed, 9, 1), N, K, 2)
+    ones = np.ones((N, K // g), dtype=np.float16)
+    y = o.gemm_ref_f64(x, c, ones, g)
+    xt = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    ref = torch.matmul(xt, torch.from_numpy(c.astype(np.float64)).T).numpy()
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_binary_is_ternary_without_zeros(o, seed=8):
+    """The same {-1,+1} codes packed as binary and as ternary decode to the same codes and
+    give identical Y."""
+    M, N, K, g = 8, 16, 128, 64
+    x = gen_x(rng_for(seed, 10, 0), M, K)
+    c = gen_codes(rng_for(seed, 10, 1), N, K, 1)
+    s = gen_scales(rng_for(seed, 10, 2), N, K, g)
+    wb, _ = o.pack(c, 1)
+    wt, _ = o.pack(c, 2)
+    cb = o.unpack(wb, K, 1)
+    ct = o.unpack(wt, K, 2)
+    assert np.array_equal(cb, c) and np.array_equal(ct, c)
+    assert np.array_equal(o.gemm_ref_f64(x, cb, s, g), o.gemm_ref_f64(x, ct, s, g))
+
+
+ALL_PINS = [pin_golden_words, pin_bitstring, pin_unpack_unused_field, pin_group_blocks, pin_one_hot, pin_fsum,
+            pin_statistics, pin_linearity, pin_library_matmul, pin_binary_is_ternary_without_zeros]

@@ -1,0 +1,186 @@
+"""The oracle against its pins, and planted mistakes that the pins must catch (CPU only)."""
+import math
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import lowbit_ref as ref
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin_holds(pin):
+    pin(P.real_oracle())
+
+
+def test_statistics_binary():
+    P.pin_statistics(P.real_oracle(), bits=1)
+
+
+def test_fsum_binary_small():
+    P.pin_fsum(P.real_oracle(), M=8, N=32, K=128, g=32, bits=1, seed=2)
+
+
+# ----------------------------------------------------------------------------------------
+# Planted mistakes: each broken oracle must fail at least one pin.
+# ----------------------------------------------------------------------------------------
+
+def _broken(**overrides):
+    o = P.real_oracle()
+    d = dict(vars(o))
+    d.update(overrides)
+    return SimpleNamespace(**d)
+
+
+def _pack_swapped_signs(codes, bits):
+    return ref.pack(-np.asarray(codes), bits) if bits == 2 else ref.pack(codes, bits)
+
+
+def _pack_msb_first(codes, bits):
+    c = np.asarray(codes)
+    per = 32 // bits
+    N, K = c.shape
+    flipped = c.reshape(N, K // per, per)[:, :, ::-1].reshape(N, K)
+    return ref.pack(flipped, bits)
+
+
+def _unpack_msb_first(words, K, bits):
+    c = ref.unpack(words, K, bits)
+    per = 32 // bits
+    N = c.shape[0]
+    return c.reshape(N, K // per, per)[:, :, ::-1].reshape(N, K)
+
+
+def _unpack_11_as_minus(words, K, bits):
+    c = ref.unpack(words, K, bits)
+    if bits == 2:
+        w = np.asarray(words, dtype=np.uint32)
+        for i in range(16):
+            f = ((w >> np.uint32(2 * i)) & np.uint32(3)) == 3
+            c.reshape(w.shape[0], w.shape[1], 16)[:, :, i][f] = -1
+    return c
+
+
+def _gemm_scale_tiled(x, codes, scales, g):
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    N, K = np.asarray(codes).shape
+    w = np.asarray(codes, dtype=np.float64) * np.tile(s, (1, g))  # k -> k % (K/g): wrong grouping
+    return ref.bf16_bits_to_f64(x) @ w.T
+
+
+def _gemm_no_scale(x, codes, scales, g):
+    return ref.bf16_bits_to_f64(x) @ np.asarray(codes, dtype=np.float64).T
+
+
+def _gemm_transposed(x, codes, scales, g):
+    c = np.asarray(codes)
+    if c.shape[0] == c.shape[1]:
+        c = c.T
+    return ref.gemm_ref_f64(x, c, scales, g)
+
+
+def _gemm_f32_accumulate(x, codes, scales, g):
+    xf = ref.bf16_bits_to_f64(x).astype(np.float32)
+    w = ref.dequant_f64(codes, scales, g).astype(np.float32)
+    return (xf @ w.T).astype(np.float64)
+
+
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _gemm_x_as_fp16(x, codes, scales, g):
+    return _bf16_as_fp16(x) @ ref.dequant_f64(codes, scales, g).T
+
+
+PLANTED = {
+    "ternary_signs_swapped": dict(pack=_pack_swapped_signs),
+    "msb_first_pack": dict(pack=_pack_msb_first),
+    "msb_first_unpack": dict(unpack=_unpack_msb_first),
+    "field11_as_minus_one": dict(unpack=_unpack_11_as_minus),
+    "scale_group_tiled": dict(gemm_ref_f64=_gemm_scale_tiled),
+    "scale_dropped": dict(gemm_ref_f64=_gemm_no_scale),
+    "square_transposed": dict(gemm_ref_f64=_gemm_transposed),
+    "fp32_accumulate": dict(gemm_ref_f64=_gemm_f32_accumulate),
+    "x_read_as_fp16": dict(gemm_ref_f64=_gemm_x_as_fp16, bf16_bits_to_f64=_bf16_as_fp16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PLANTED))
+def test_planted_mistake_is_caught(name):
+    broken = _broken(**PLANTED[name])
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every pin"
+
+
+# ----------------------------------------------------------------------------------------
+# Number-format helpers and the acceptance check
+# ----------------------------------------------------------------------------------------
+
+def test_bf16_widening_known_values():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0x0000, 0x8000, 0x4000], dtype=np.uint16)
+    want = [1.0, -1.0, 3.140625, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 0.0, -0.0, 2.0]
+    got = oracle.bf16_bits_to_f64(bits)
+    assert list(got) == want
+
+
+def test_bf16_rounding_known_values():
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -2.5, 0.0,
+                     2.0 ** -133, 1.5 * 2.0 ** -133, 3.5e38])
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x0000, 0x0001, 0x0002, 0x7F80]
+    assert [int(b) for b in oracle.f64_to_bf16_bits_rne(vals)] == want
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))
+    ours = oracle.f64_to_bf16_bits_rne(v)
+    # torch rounds float32 -> bfloat16 to nearest even; go through float32 only where that
+    # first rounding is exact (values with <= 24 significant bits)
+    v32 = v.astype(np.float32).astype(np.float64)
+    theirs = torch.from_numpy(v32).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_bits_rne(v32), theirs)
+    assert ours.shape == v.shape
+
+
+def test_tolerance_check():
+    rng = np.random.default_rng(2)
+    yref = rng.standard_normal((64, 64)) * 2
+    yb = oracle.f64_to_bf16_bits_rne(yref)
+    r = oracle.check_tolerance(yb, yref)
+    assert r["ok"] and r["rel_frob"] < 2.5e-3
+    bad = yref.copy()
+    bad[3, 4] += 0.011 * (abs(yref[3, 4]) + 1)
+    assert not oracle.check_tolerance(bad, yref)["ok"]
+    nan = yref.copy()
+    nan[0, 0] = math.nan
+    assert not oracle.check_tolerance(nan, yref)["ok"]
+
+
+def test_invalid_codes_counted():
+    c = np.array([[0, 1, -1, 2, -2, 5, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0]], dtype=np.int8)
+    w, bad = oracle.pack(c, 2)
+    assert bad == 3
+    assert np.array_equal(oracle.unpack(w, 16, 2)[0], np.where(np.isin(c[0], [-1, 0, 1]), c[0], 0))
+    cb = np.ones((1, 32), dtype=np.int8)
+    cb[0, 4] = 0
+    cb[0, 9] = 3
+    wb, badb = oracle.pack(cb, 1)
+    assert badb == 2 and int(wb[0, 0]) == 0xFFFFFFFF & ~((1 << 4) | (1 << 9))
+
+
+def test_roundtrip_large():
+    from workloads import gen_codes, rng_for
+    for bits in (1, 2):
+        c = gen_codes(rng_for(0, 50, bits), 96, 1024, bits)
+        w, bad = oracle.pack(c, bits)
+        assert bad == 0 and w.shape == (96, 1024 * bits // 32)
+        assert np.array_equal(oracle.unpack(w, 1024, bits), c)

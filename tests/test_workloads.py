@@ -1,0 +1,44 @@
+"""Sanity of the seeded input generators (CPU only)."""
+import numpy as np
+
+import workloads as W
+
+
+def test_x_is_bf16_rne_of_normal():
+    import torch
+    rng = W.rng_for(0, 1, 0)
+    x = W.gen_x(rng, 64, 512)
+    ref = W.rng_for(0, 1, 0).standard_normal((64, 512), dtype=np.float32)
+    t = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(x, t)
+
+
+def test_code_distributions():
+    c = W.gen_codes(W.rng_for(0, 1, 1), 512, 1024, W.TERNARY)
+    frac = [(c == v).mean() for v in (-1, 0, 1)]
+    assert abs(frac[0] - 0.25) < 0.01 and abs(frac[1] - 0.5) < 0.01 and abs(frac[2] - 0.25) < 0.01
+    b = W.gen_codes(W.rng_for(0, 2, 1), 512, 1024, W.BINARY)
+    assert set(np.unique(b)) == {-1, 1} and abs((b == 1).mean() - 0.5) < 0.01
+
+
+def test_scales_range():
+    s = W.gen_scales(W.rng_for(0, 1, 2), 256, 3072, 64)
+    assert s.dtype == np.float16 and s.shape == (256, 48)
+    assert s.min() >= np.float16(0.005) and s.max() <= np.float16(0.05)
+
+
+def test_seeded_and_distinct():
+    p = W.Problem("a", 8, 32, 128)
+    a, b = W.make_inputs(p), W.make_inputs(p)
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.codes, b.codes)
+    q = W.Problem("b", 8, 32, 128, tensor_id=1)
+    assert not np.array_equal(W.make_inputs(q).codes, a.codes)
+
+
+def test_denoise_step_sweep_shape_count():
+    probs = W.denoise_step_sweep()
+    assert len(probs) == 80
+    flops = sum(p.flops for p in probs)
+    assert abs(flops / 1e12 - 28.27) < 0.01
+    skinny = W.denoise_step_sweep(skinny_m=16)
+    assert all(p.M == 16 for p in skinny) and len(skinny) == 80
