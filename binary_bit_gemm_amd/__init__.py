@@ -1,0 +1,165 @@
+"""binary_bit_gemm_amd -- packed ternary / binary weight GEMM for AMD MI355X (gfx950).
+
+Thin ctypes binding over liblowbit.so (include/lowbit.h).  Every step of the computation
+runs in the library's HIP kernels; this module only checks tensor types, takes device
+pointers and the current HIP stream, and raises on a non-zero status.  PyTorch is used for
+device memory and streams only.
+
+    import torch, binary_bit_gemm_amd as lb
+    words, bad = lb.pack(codes_int8_cuda, bits=2)          # [N, K] -> [N, K/16] (int32 view)
+    y = lb.gemm(x_bf16_cuda, words, scales_fp16_cuda, g=64, bits=2)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+from ._lib import LowbitError, lib, library_path  # noqa: F401
+
+TERNARY = 2
+BINARY = 1
+MAX_BATCH = 64
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.lowbit_status_string(status).decode()
+        hip = L.lowbit_last_hip_error()
+        raise LowbitError(status, f"{what}: {msg}" + (f" (hipError {hip})" if status == 4 else ""))
+
+
+def _require(t, dtype, name: str, ndim: int = 2):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def words_per_row(K: int, bits: int) -> int:
+    return K * bits // 32
+
+
+def pack(codes, bits: int, count_invalid: bool = True) -> Tuple["object", Optional[int]]:
+    """int8 codes [N, K] on the GPU -> (packed words [N, K*bits/32] as int32, invalid count).
+
+    The invalid count (codes outside {-1,0,1} / {-1,1}) is read back only when
+    count_invalid is true (that synchronises the stream)."""
+    torch = _torch()
+    _require(codes, torch.int8, "codes")
+    N, K = codes.shape
+    words = torch.empty((N, words_per_row(K, bits)), dtype=torch.int32, device=codes.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if count_invalid else None
+    st = lib().lowbit_pack(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(words.data_ptr()), N, K, bits,
+                           ctypes.c_void_p(bad.data_ptr() if bad is not None else 0),
+                           ctypes.c_void_p(_stream_ptr(codes.device)))
+    _check(st, "lowbit_pack")
+    return words, (int(bad.item()) if bad is not None else None)
+
+
+def unpack(words, K: int, bits: int):
+    """Packed words [N, K*bits/32] -> int8 codes [N, K]."""
+    torch = _torch()
+    _require(words, torch.int32, "words")
+    N = words.shape[0]
+    if words.shape[1] != words_per_row(K, bits):
+        raise ValueError("words do not hold K codes per row")
+    codes = torch.empty((N, K), dtype=torch.int8, device=words.device)
+    st = lib().lowbit_unpack(ctypes.c_void_p(words.data_ptr()), ctypes.c_void_p(codes.data_ptr()), N, K, bits,
+                             ctypes.c_void_p(_stream_ptr(words.device)))
+    _check(st, "lowbit_unpack")
+    return codes
+
+
+def gemm(x, words, scales, g: int, bits: int, out=None):
+    """Y[M, N] = X[M, K] . dequant(W)[N, K]^T in bf16 (see include/lowbit.h)."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    _require(words, torch.int32, "words")
+    _require(scales, torch.float16, "scales")
+    M, K = x.shape
+    N = words.shape[0]
+    if words.shape[1] != words_per_row(K, bits):
+        raise ValueError(f"words must be [N, K*bits/32] = [{N}, {words_per_row(K, bits)}], got {tuple(words.shape)}")
+    if K % g or tuple(scales.shape) != (N, K // g):
+        raise ValueError(f"scales must be [N, K/g] = [{N}, {K // g if g else 0}], got {tuple(scales.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().lowbit_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                           ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                           M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
+    _check(st, "lowbit_gemm")
+    return out
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("W", ctypes.c_void_p), ("S", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("g", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+def gemm_batched(problems: Sequence[Tuple["object", "object", "object", "object", int, int]]) -> None:
+    """Run independent GEMMs [(x, words, scales, out, g, bits), ...] as grouped launches.
+    Outputs are written in place; all tensors on the same device."""
+    torch = _torch()
+    if len(problems) > MAX_BATCH:
+        raise ValueError(f"at most {MAX_BATCH} problems per call")
+    arr = (Problem * max(1, len(problems)))()
+    dev = None
+    for i, (x, w, s, y, g, bits) in enumerate(problems):
+        _require(x, torch.bfloat16, "x")
+        _require(w, torch.int32, "words")
+        _require(s, torch.float16, "scales")
+        _require(y, torch.bfloat16, "out")
+        M, K = x.shape
+        N = w.shape[0]
+        if w.shape[1] != words_per_row(K, bits) or tuple(s.shape) != (N, K // g) or tuple(y.shape) != (M, N):
+            raise ValueError(f"problem {i}: inconsistent shapes")
+        dev = x.device
+        arr[i] = Problem(x.data_ptr(), w.data_ptr(), s.data_ptr(), y.data_ptr(), M, N, K, g, bits)
+    if not problems:
+        return
+    st = lib().lowbit_gemm_batched(arr, len(problems), ctypes.c_void_p(_stream_ptr(dev)))
+    _check(st, "lowbit_gemm_batched")
+
+
+def check_gemm_args(x_ptr: int, w_ptr: int, s_ptr: int, y_ptr: int, M: int, N: int, K: int, g: int,
+                    bits: int) -> int:
+    """Host-only validation (no HIP call); returns the status code lowbit_gemm would return."""
+    return lib().lowbit_check_gemm_args(ctypes.c_void_p(x_ptr), ctypes.c_void_p(w_ptr), ctypes.c_void_p(s_ptr),
+                                        ctypes.c_void_p(y_ptr), M, N, K, g, bits)
+
+
+def variant(M: int, N: int, K: int, g: int = 64, bits: int = 2) -> str:
+    """Name of the kernel variant lowbit_gemm picks for this shape."""
+    return lib().lowbit_gemm_variant(M, N, K, g, bits).decode()
+
+
+def status_string(status: int) -> str:
+    return lib().lowbit_status_string(status).decode()
+
+
+def version() -> int:
+    return lib().lowbit_version()

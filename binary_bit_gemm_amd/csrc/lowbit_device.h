@@ -1,0 +1,88 @@
+// Device-side building blocks of the low-bit GEMM kernels (gfx950 only).
+//
+// Weight codes are expanded in registers into bf16 MFMA operand dwords.  Each dword holds
+// two consecutive codes k, k+1 as a bf16 pair (lo half = code k).  The value of a code c is
+// written as 2*c (ternary) or -2*c (binary): +-2.0 has a zero low byte (0x4000 / 0xC000),
+// so only the high byte of every bf16 has to be produced, and the factor +-1/2 is folded
+// exactly into the fp32 group scale that multiplies each group's partial sum after the MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+// v_perm_b32: byte i of the result is byte sel.byte[i] of the 8-byte value {hi:lo}
+// (0..3 -> lo, 4..7 -> hi); selector 0x0C yields 0x00.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Selector that builds the bf16 pair [0x00, lo.byte[b], 0x00, hi.byte[b]].
+__device__ __forceinline__ constexpr uint32_t pair_sel(int b) {
+    return 0x0Cu | (uint32_t(b) << 8) | (0x0Cu << 16) | (uint32_t(4 + b) << 24);
+}
+
+// Ternary word (16 codes, 2-bit fields 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0) to 8 operand
+// dwords; out[d] = bf16 pair (2*c[2d], 2*c[2d+1]).
+//   e_r  = fields r, r+4, r+8, r+12 moved to the low bits of bytes 0..3
+//   l_r  = table lookup of each byte: 0 -> 0x00, 1 -> 0x40, 2 -> 0xC0, 3 -> 0x00
+//   out  = byte gathers from l_r (codes 4b+r sit in byte b of l_r)
+__device__ __forceinline__ void expand_ternary_word(uint32_t w, uint32_t out[8]) {
+    constexpr uint32_t kHighByte = 0x00C04000u;
+    const uint32_t e0 = w & 0x03030303u;
+    const uint32_t e1 = (w >> 2) & 0x03030303u;
+    const uint32_t e2 = (w >> 4) & 0x03030303u;
+    const uint32_t e3 = (w >> 6) & 0x03030303u;
+    const uint32_t l0 = perm_b32(kHighByte, kHighByte, e0);
+    const uint32_t l1 = perm_b32(kHighByte, kHighByte, e1);
+    const uint32_t l2 = perm_b32(kHighByte, kHighByte, e2);
+    const uint32_t l3 = perm_b32(kHighByte, kHighByte, e3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        out[2 * b] = perm_b32(l1, l0, pair_sel(b));
+        out[2 * b + 1] = perm_b32(l3, l2, pair_sel(b));
+    }
+}
+
+// Binary word (32 codes, bit 1 -> +1, bit 0 -> -1) to 16 operand dwords;
+// out[d] = bf16 pair (-2*c[2d], -2*c[2d+1]).  NOUT < 16 expands only the low 2*NOUT codes.
+//   e_j = byte b holds 0x40 | bit(8b+j) << 7, i.e. +2.0 for bit 0 and -2.0 for bit 1
+template <int NOUT = 16>
+__device__ __forceinline__ void expand_binary_word(uint32_t w, uint32_t out[NOUT]) {
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = ((w << (7 - j)) & 0x80808080u) | 0x40404040u;
+#pragma unroll
+    for (int d = 0; d < NOUT; ++d) {
+        const int b = d >> 2, j = 2 * (d & 3);
+        out[d] = perm_b32(e[j + 1], e[j], pair_sel(b));
+    }
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite and infinite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Hardware workgroup id -> tile id, so that the tiles one XCD runs are contiguous in tile
+// order.  Workgroups are dealt to the 8 XCDs round-robin (id % 8); XCD x gets the tile
+// range [start(x), start(x) + count(x)).
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+    constexpr int kXcd = 8;
+    const int x = pid % kXcd, slot = pid / kXcd;
+    const int base = total / kXcd, extra = total % kXcd;
+    return x * base + (x < extra ? x : extra) + slot;
+}
+
+}  // namespace lowbit

@@ -1,0 +1,36 @@
+// Internal declarations shared by the HIP translation units of liblowbit (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+struct GemmProblem {
+    const uint16_t* X;  // bf16 [M, K]
+    const uint32_t* W;  // packed codes [N, K*bits/32]
+    const uint16_t* S;  // fp16 [N, K/g]
+    uint16_t* Y;        // bf16 [M, N]
+    int M, N, K;
+};
+
+hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
+                       int32_t* bad_count, hipStream_t stream);
+hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
+                         hipStream_t stream);
+
+// Large-M tile kernel (MFMA, LDS-staged X).  `variant` selects the tile shape.
+enum TileVariant { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x128 = 2 };
+hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
+
+// Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
+hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream);
+
+// Grouped launch: several problems of the same (g, bits) in one persistent launch.
+hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int bits,
+                               hipStream_t stream);
+
+int pick_tile_variant(int64_t M, int64_t N, int64_t K);
+bool use_skinny(int64_t M, int64_t N, int64_t K);
+
+}  // namespace lowbit

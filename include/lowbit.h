@@ -1,0 +1,140 @@
+/*
+ * lowbit.h -- packed low-bit weight GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for bf16 activations X and packed ternary or binary weights W
+ * with fp16 group scales S,
+ *
+ *     Y[m, n] = sum_k  X[m, k] * c[n, k] * S[n, k / g]              (Y in bf16)
+ *
+ * which is the linear layer of the Bonsai-quantised FLUX.2 Klein 4B diffusion
+ * transformer:
+ *   - binary weights w = scale_g * b, b in {-1, +1}, one fp16 scale per group of g
+ *     consecutive weights ("bonsai-image-binary-4B-gemlite-1bit" model card, section
+ *     "Binary Weight Representation: 1-bit g128"; the same card's "Model Overview" lists
+ *     the binary values + FP16 group-wise scales weight format);
+ *   - ternary weights {-1, 0, +1} in 2 bits, multiplied by a 2-bit quantised matmul
+ *     (mlx-vlm Prism Bonsai ternary 2-bit guide, section 运行前提 / prerequisites);
+ *   - weights kept as packed uint32 words plus scales ("backend/ -- FastAPI Mac backend",
+ *     section "Checkpoint layout").
+ *
+ * ---------------------------------------------------------------------------------
+ * Packed weight format (the pages leave the bit layout open; this is the library's):
+ *   ternary (bits = 2): 16 codes per uint32, along K, least significant field first:
+ *       code k of row n is the 2-bit field at bits 2*(k%16) .. 2*(k%16)+1 of
+ *       W[n * (K/16) + k/16];  field 00 -> 0, 01 -> +1, 10 -> -1.  The field 11 is never
+ *       written; readers decode it as 0.
+ *   binary  (bits = 1): 32 codes per uint32, along K: code k of row n is bit k%32 of
+ *       W[n * (K/32) + k/32];  1 -> +1, 0 -> -1.
+ *   scales: fp16 (IEEE binary16) S[n * (K/g) + k/g], symmetric (no zero point).
+ * Activations X[M, K] and outputs Y[M, N] are bf16, row-major, contiguous.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is enqueued
+ *     asynchronously; nothing synchronises the host.  Device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a non-zero
+ *     return means nothing was launched.
+ *   - Supported: bits in {1, 2}; g in {32, 64, 128}; K % g == 0; N % 16 == 0; M >= 0
+ *     (M == 0 or N == 0 is a no-op); M, N, K < 2^31; the current device is gfx950.
+ *   - The library allocates no device memory and uses no hidden workspace.
+ *   - Results are deterministic: the same inputs give bitwise the same Y on every run.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_VERSION 100 /* 1.0.0 */
+
+/* Status codes returned by every entry point. */
+enum {
+    LOWBIT_OK = 0,
+    LOWBIT_E_INVALID = 1,     /* null pointer, negative size, N % 16 or K % g != 0 ...     */
+    LOWBIT_E_UNSUPPORTED = 2, /* bits / g outside the supported set, or device not gfx950  */
+    LOWBIT_E_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned                   */
+    LOWBIT_E_HIP = 4,         /* a HIP runtime call failed; see lowbit_last_hip_error()    */
+    LOWBIT_E_TOO_MANY = 5     /* batched call: more problems than one call accepts         */
+};
+
+/*
+ * lowbit_pack -- int8 codes [N, K] -> packed words [N, K*bits/32] in the format above.
+ *   codes       device, N*K int8, row-major.  Ternary expects {-1,0,1}, binary {-1,1}.
+ *   W           device, N*K*bits/32 uint32, written.
+ *   bad_count   device int32 or NULL.  When given, the number of codes outside the
+ *               valid set is ADDED to *bad_count (the caller zeroes it); such codes are
+ *               packed as 0 bits (ternary 0, binary -1).
+ *   Requires K % (32/bits) == 0.  This is the offline, load-time step.
+ */
+int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
+                int32_t* bad_count, void* stream);
+
+/*
+ * lowbit_unpack -- packed words -> int8 codes [N, K] (ternary field 11 -> 0).
+ */
+int lowbit_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits, void* stream);
+
+/*
+ * lowbit_gemm -- Y[M, N] = X[M, K] . dequant(W)[N, K]^T, bf16 out (round to nearest even).
+ *   X  device bf16 [M, K];  W  device packed words [N, K*bits/32];
+ *   S  device fp16 [N, K/g];  Y  device bf16 [M, N], fully overwritten.
+ * The weight codes are expanded to bf16 in registers and multiplied on the bf16 matrix
+ * cores with fp32 accumulation; each group's partial sum is multiplied by its fp32 scale
+ * after the matrix multiply (the scale is not rounded to bf16).  The kernel is chosen
+ * from M (skinny M uses split-K inside a workgroup, reduced in a fixed order).
+ */
+int lowbit_gemm(const void* X, const uint32_t* W, const void* S, void* Y,
+                int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
+
+/* One problem of a batched call: the same meaning as the lowbit_gemm arguments. */
+typedef struct lowbit_problem {
+    const void* X;
+    const uint32_t* W;
+    const void* S;
+    void* Y;
+    int64_t M, N, K;
+    int32_t g, bits;
+} lowbit_problem;
+
+#define LOWBIT_MAX_BATCH 64
+
+/*
+ * lowbit_gemm_batched -- `count` independent GEMMs in one launch per (bits, g) class.
+ *   problems  HOST array of `count` problems (read before return; may be freed after).
+ * Intended for the independent linears of one transformer block (e.g. the image and text
+ * streams' QKV of a double-stream block), so that small-M and small-N problems share the
+ * machine.  Problems must not write overlapping Y.  count <= LOWBIT_MAX_BATCH.
+ * Every problem is validated as in lowbit_gemm before anything is launched.
+ */
+int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream);
+
+/* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
+ * would return before touching the device. */
+int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,
+                           int64_t M, int64_t N, int64_t K, int g, int bits);
+
+/* Name of the kernel variant lowbit_gemm picks for a shape (for logs and tests). */
+const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
+
+/* Human-readable text for a status code. */
+const char* lowbit_status_string(int status);
+
+/* hipError_t of the last failed HIP call in this thread (0 if none). */
+int lowbit_last_hip_error(void);
+
+/* 1 if `device` is a gfx950 GPU the library can run on, 0 if not, -LOWBIT_E_HIP on error. */
+int lowbit_device_supported(int device);
+
+/* LOWBIT_VERSION of the built library. */
+int lowbit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

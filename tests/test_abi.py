@@ -1,0 +1,92 @@
+"""The C-ABI library loads, exports every declared entry point, and validates arguments on
+the host without touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import binary_bit_gemm_amd as lb
+from binary_bit_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowbit.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, HIP, TOO_MANY = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lowbit_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("lowbit_pack", "lowbit_unpack", "lowbit_gemm", "lowbit_gemm_batched"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES), "binding signatures out of date"
+
+
+def test_version_and_status_strings():
+    assert lb.version() == 100
+    for s in (OK, INVALID, UNSUPPORTED, ALIGN, HIP, TOO_MANY):
+        assert lb.status_string(s) and lb.status_string(s) != "unknown status"
+    assert lb.status_string(99) == "unknown status"
+
+
+A = 0x10000  # a 16-byte-aligned fake address: never dereferenced by the host checks
+
+
+@pytest.mark.parametrize("args,want", [
+    ((A, A, A, A, 64, 256, 256, 64, 2), OK),
+    ((A, A, A, A, 64, 256, 256, 64, 3), UNSUPPORTED),        # bits
+    ((A, A, A, A, 64, 256, 256, 48, 2), UNSUPPORTED),        # g
+    ((A, A, A, A, 64, 256, 256, 16, 1), UNSUPPORTED),
+    ((A, A, A, A, 64, 250, 256, 64, 2), INVALID),            # N % 16
+    ((A, A, A, A, 64, 256, 200, 64, 2), INVALID),            # K % g
+    ((A, A, A, A, -1, 256, 256, 64, 2), INVALID),
+    ((A, A, A, A, 64, 256, 1 << 31, 64, 2), INVALID),
+    ((0, A, A, A, 64, 256, 256, 64, 2), INVALID),            # null X
+    ((A, 0, A, A, 64, 256, 256, 64, 2), INVALID),
+    ((A, A, 0, A, 64, 256, 256, 64, 2), INVALID),
+    ((A, A, A, 0, 64, 256, 256, 64, 2), INVALID),
+    ((A + 8, A, A, A, 64, 256, 256, 64, 2), ALIGN),
+    ((A, A + 4, A, A, 64, 256, 256, 64, 2), ALIGN),
+    ((A, A, A + 2, A, 64, 256, 256, 64, 2), ALIGN),
+    ((A, A, A, A + 2, 64, 256, 256, 64, 2), ALIGN),
+    ((0, 0, 0, 0, 0, 256, 256, 64, 2), OK),                   # M == 0: nothing to do
+    ((0, 0, 0, A, 64, 256, 0, 64, 2), OK),                    # K == 0: Y = 0, no inputs read
+    ((A, A, A, A, 64, 256, 256, 128, 1), OK),
+    ((A, A, A, A, 64, 256, 256, 32, 1), OK),
+])
+def test_check_gemm_args(args, want):
+    assert lb.check_gemm_args(*args) == want
+
+
+def test_gemm_rejects_before_touching_the_device():
+    L = _lib.lib()
+    st = L.lowbit_gemm(A, A, A, A, 64, 250, 256, 64, 2, None)
+    assert st == INVALID
+    st = L.lowbit_pack(A, A, 16, 24, 2, None, None)  # K not a multiple of 16
+    assert st == INVALID
+    st = L.lowbit_unpack(A, A, 16, 32, 5, None)
+    assert st == UNSUPPORTED
+    probs = (lb.Problem * 2)()
+    probs[0] = lb.Problem(A, A, A, A, 64, 256, 256, 64, 2)
+    probs[1] = lb.Problem(A, A, A, A, 64, 256, 256, 64, 7)
+    assert L.lowbit_gemm_batched(probs, 2, None) == UNSUPPORTED
+    assert L.lowbit_gemm_batched(probs, lb.MAX_BATCH + 1, None) == TOO_MANY
+    assert L.lowbit_gemm_batched(None, 3, None) == INVALID
+    assert L.lowbit_gemm_batched(None, 0, None) == OK
+
+
+def test_variant_choice():
+    assert lb.variant(4608, 18432, 3072).startswith("tile")
+    assert lb.variant(64, 256, 256) in ("tile64x128", "skinny")
