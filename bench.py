@@ -1,0 +1,197 @@
+"""Throughput of the packed low-bit weight GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload res1024|res512|res512_binary|sweep|skinny]
+
+A step is one pass of the hot path over one batch of synthetic inputs that are already
+resident in HBM: every GEMM of the workload, each with its own weights.  Packing is the
+offline load-time step and runs before the timed region.
+
+Workloads (FLUX.2 Klein 4B MMDiT linears, hidden 3072):
+  res1024        M = 4608 tokens (4096 image + 512 text) ternary g=64:
+                 N x K = 3072x3072, 9216x3072, 18432x3072, 3072x9216, 3072x12288   (default)
+  res512         M = 1536, the first four shapes, ternary g=64
+  res512_binary  the same, binary g=64
+  sweep          the 80 quantised GEMMs of one denoise step at 1024x1024
+  skinny         the same 80 GEMMs at M = 16 (HBM-bound; reports GB/s)
+
+Prints one JSON line.  Inputs are seeded and synthetic: X ~ N(0,1) -> bf16, codes i.i.d.
+ternary {-1:.25, 0:.5, +1:.25} (binary {-1,+1} at .5), scales U[0.005, 0.05] -> fp16.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "lowbit GEMM TFLOP/s and % of bf16 MFMA peak (M=4608, ternary g=64)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="res1024",
+                    choices=["res1024", "res512", "res512_binary", "sweep", "skinny"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of X in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def problems_for(workload):
+    import workloads as W
+    if workload == "res1024":
+        return W.RES1024_TERNARY
+    if workload == "res512":
+        return W.RES512_TERNARY
+    if workload == "res512_binary":
+        return W.RES512_BINARY
+    if workload == "sweep":
+        return W.denoise_step_sweep()
+    if workload == "skinny":
+        return W.denoise_step_sweep(skinny_m=16)
+    raise ValueError(workload)
+
+
+def make_device_inputs(probs, seed):
+    """Seeded synthetic inputs drawn on the device (same distributions as workloads.py),
+    codes packed with lowbit_pack (load-time, untimed)."""
+    import torch
+    import binary_bit_gemm_amd as lb
+    gen = torch.Generator(device="cuda")
+    lut = torch.tensor([-1, 0, 0, 1], dtype=torch.int8, device="cuda")
+    bufs = []
+    for i, p in enumerate(probs):
+        gen.manual_seed(seed * 1000003 + p.config_id * 1009 + p.tensor_id)
+        x = torch.randn((p.M, p.K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        if p.bits == 2:
+            codes = lut[torch.randint(0, 4, (p.N, p.K), generator=gen, device="cuda")]
+        else:
+            codes = (torch.randint(0, 2, (p.N, p.K), generator=gen, device="cuda", dtype=torch.int8) * 2 - 1)
+        words, _ = lb.pack(codes.contiguous(), p.bits, count_invalid=False)
+        del codes
+        s = (torch.rand((p.N, p.K // p.g), generator=gen, device="cuda") * 0.045 + 0.005).to(torch.float16)
+        y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+        bufs.append((x, words, s, y, p.g, p.bits))
+    torch.cuda.synchronize()
+    return bufs
+
+
+def cpu_baseline(probs, rows, seed):
+    """The oracle as it stands (unpack, fp64 dequantise, numpy matmul) on the first `rows`
+    rows of X for every distinct shape of the workload, on the host's cores."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    seen = {}
+    for p in probs:
+        seen.setdefault((p.N, p.K, p.bits, p.g), p)
+    flops = 0
+    elapsed = 0.0
+    for (N, K, bits, g), p in seen.items():
+        m = min(rows, p.M)
+        q = W.Problem(p.name, m, N, K, bits, g, p.config_id, p.tensor_id)
+        inp = W.make_inputs(q, seed)
+        words, _ = oracle.pack(inp.codes, bits)
+        t0 = time.perf_counter()
+        oracle.gemm_ref_from_words(inp.x, words, inp.scales, K, g, bits)
+        elapsed += time.perf_counter() - t0
+        flops += 2 * m * N * K
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} rows of X for each of the {len(seen)} distinct (N, K) shapes; "
+                      f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import binary_bit_gemm_amd as lb
+
+    probs = problems_for(a.workload)
+    bufs = make_device_inputs(probs, a.seed)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, (x, w, s, y, g, bits) in enumerate(bufs):
+            if events is not None:
+                events[i][0].record(stream)
+            lb.gemm(x, w, s, g, bits, out=y)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, wall clock between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-launch kernel durations with HIP events on the launch stream (separate pass)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in bufs]
+          for _ in range(a.steps)]
+    for k in range(a.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    launch_ms = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(a.steps)) / a.steps
+                 for i in range(len(bufs))]
+
+    flops_step = sum(p.flops for p in probs)
+    bytes_step = sum(p.bytes_moved() for p in probs)
+    ms_per_step = elapsed * 1e3 / a.steps
+    tflops = flops_step / (elapsed / a.steps) / 1e12
+    kern_ms = sum(launch_ms)
+    kern_tflops = flops_step / (kern_ms * 1e-3) / 1e12
+    kern_gbs = bytes_step / (kern_ms * 1e-3) / 1e9
+
+    if a.workload == "skinny":
+        metric, value, unit = "lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)", \
+            bytes_step / (elapsed / a.steps) / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        metric = METRIC if a.workload == "res1024" else METRIC.replace("(M=4608, ternary g=64)", f"({a.workload})")
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
+    out = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "gemms_per_step": len(probs),
+                   "shapes": sorted({f"{p.M}x{p.N}x{p.K}" for p in probs}),
+                   "bits": sorted({p.bits for p in probs}), "g": sorted({p.g for p in probs}),
+                   "flop_per_step": flops_step, "bytes_per_step": bytes_step,
+                   "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                   "kernel_variants": variants,
+                   "per_gemm_us": [round(1e3 * t, 2) for t in launch_ms[:8]]},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA results in ordinary VGPRs: the per-group scale FMA reads every MFMA
+          # result, and AGPR results would cost one v_accvgpr_read per element
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -1,64 +1,109 @@
-// Large-M packed low-bit GEMM: Y[M,N] = X[M,K] . dequant(W)[N,K]^T on the gfx950 matrix cores.
+// Packed low-bit GEMM on the gfx950 matrix cores: Y[M,N] = X[M,K] . dequant(W)[N,K]^T.
 //
-// Workgroup = 4 waves (256 threads) computing a BM x BN tile of Y; each wave owns a
-// WM x WN sub-tile made of 32x32 blocks (v_mfma_f32_32x32x16_bf16).  Per K step of
-// KS = max(64, g) elements:
-//   * X[BM, KS] is copied HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4),
-//     double-buffered, 16-byte chunks XOR-swizzled by row to keep ds_read_b128 conflict-free;
-//   * every lane loads the packed words of its own weight row (one column of Y) straight
-//     into registers, together with that row's fp16 group scales, one step ahead;
-//   * codes are expanded in registers to bf16 operand dwords (lowbit_device.h);
-//   * per scale group: tmp = sum of g/16 MFMAs, then acc += scale * tmp in fp32 -- the
-//     group scale multiplies the exact partial sum after the MFMA and is never rounded
-//     to bf16 (w = scale_g * b of the binary model card, applied per group);
-//   * epilogue: fp32 -> bf16 round-to-nearest-even, store.
+// Tiles of BM x BN outputs per workgroup; each wave owns WM x WN of them as 32x32 blocks
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  The K loop advances 64 elements per step.
 //
-// Which 8 of a group's codes a lane feeds to one MFMA is a free choice as long as the A
-// (activation) and B (weight) operands agree: lane half h (lanes 32h..32h+31) takes the
-// h-th half of each group, chunk j takes codes 8j..8j+7 of that half.  Consecutive codes
-// in K therefore meet consecutive activations, so X tiles need no reordering.
+// Data movement is organised around the vector-memory (texture address) path, whose
+// per-request cost is what limits a kernel whose math is cheap per byte: a wave that finds
+// that path's queue full cannot issue its next instruction, MFMAs included.  Everything
+// therefore moves in large contiguous pieces through direct-to-LDS buffer loads:
+//   * X[BM, 64] per step, double-buffered (rows past M read as zero);
+//   * packed weights in blocks of 64 bytes per weight row (4 steps of ternary codes,
+//     8 of binary), double-buffered;
+//   * fp16 scales in blocks of 8 groups per weight row, double-buffered.
+// All LDS tiles are XOR-swizzled in 16-byte chunks so that the operand reads are free of
+// bank conflicts.
+//
+// Per step each wave expands, in registers, the codes of its own WN weight rows to bf16
+// operands (lowbit_device.h; each code is expanded once per wave and reused by WM/32 MFMA
+// blocks), runs for every scale group tmp = sum of g/16 (at most 4) MFMAs and folds the
+// group scale in after the MFMA: acc += scale * tmp in fp32 -- the fp16 scale multiplies the
+// exact partial sum and is never rounded to bf16 (w = scale_g * b, model card "Binary Weight
+// Representation: 1-bit g128").  A group of 128 spans two steps and its scale is applied to
+// each 64-element half.  Epilogue: fp32 -> bf16 round-to-nearest-even.
+//
+// The K positions a lane feeds to one MFMA are a free choice as long as the activation and
+// weight operands agree: lane half h takes the h-th half of every scale group (or of every
+// 64-element step), chunk j its codes 8j..8j+7, so consecutive codes meet consecutive
+// activations and X needs no reordering.
 #include "lowbit_device.h"
 #include "lowbit_internal.h"
 
 namespace lowbit {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, gfx9 family
+constexpr int KS = 64;                    // K elements per step
+constexpr int kRowBytes = KS * 2;         // one bf16 row of an X tile
+constexpr int kChunksPerRow = KS / 8;     // 16-byte chunks per X row
 
-template <int BITS, int G, int BM, int BN, int WAVES_M>
-struct TileCfg {
-    static constexpr int WAVES_N = kWaves / WAVES_M;
-    static constexpr int WM = BM / WAVES_M;
-    static constexpr int WN = BN / WAVES_N;
-    static constexpr int MB = WM / 32;                 // 32-row blocks per wave
-    static constexpr int NB = WN / 32;                 // 32-col blocks per wave
-    static constexpr int KS = G > 64 ? G : 64;         // K elements per step
-    static constexpr int GPS = KS / G;                 // scale groups per step
-    static constexpr int CHUNKS = G / 16;              // MFMAs per group per block
-    static constexpr int ROW_BYTES = KS * 2;           // bf16 row of the X tile
-    static constexpr int TILE_BYTES = BM * ROW_BYTES;
-    static constexpr int CHUNKS_PER_ROW = KS / 8;      // 16-byte chunks per X row
-    static constexpr int LOADS = TILE_BYTES / (16 * kThreads);  // global_load_lds per thread per step
-    // Packed words of one lane-half of one group: G/2 codes.
-    static constexpr int WPH = (G / 2) * BITS / 32 > 0 ? (G / 2) * BITS / 32 : 1;
-    static constexpr bool HALF_WORD = (G / 2) * BITS < 32;  // binary g = 32: 16 codes per half
-    static_assert(MB >= 1 && NB >= 1, "wave tile too small");
-    static_assert(TILE_BYTES % (16 * kThreads) == 0, "tile not a whole number of loads");
-};
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ __forceinline__ int lds_offset(int row, int chunk, int row_bytes) {
-    return row * row_bytes + ((chunk ^ (row & 7)) << 4);
+// Buffer resource with its fields forced into scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, int(n),
+                                             kBufferFlags);
 }
 
-template <int BITS, int G, int BM, int BN, int WAVES_M>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmProblem p, int tiles_m, int tiles_n) {
-    using C = TileCfg<BITS, G, BM, BN, WAVES_M>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// 16-byte direct-to-LDS copy; the wave's 64 lanes land at consecutive 16-byte slots from
+// lds_wave_base.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                            soff, 0, 0);
+}
+
+__device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
+
+// Packed-weight block: 64 bytes per row = four 16-byte chunks; chunk c of row r is stored at
+// position c ^ ((r >> 2) & 3) so that 16 consecutive rows reading the same chunk hit 16
+// different bank groups.
+__device__ __forceinline__ int w_swz(int row) { return (row >> 2) & 3; }
+
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+struct Cfg {
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int MB = WM / 32, NB = WN / 32;
+    static constexpr int SUBG = G < KS ? G : KS;             // K elements per scale application
+    static constexpr int GPS = KS / SUBG;                    // scale applications per step
+    static constexpr int CHUNKS = SUBG / 16;                 // MFMAs per application per block
+    static constexpr int X_TILE = BM * kRowBytes;
+    static constexpr int X_LOADS = X_TILE / (16 * THREADS);  // 16-byte copies per thread per step
+    static constexpr int W_STEP_BYTES = KS * BITS / 8;       // packed bytes of one row per step
+    static constexpr int W_SPB = 64 / W_STEP_BYTES;          // steps per 64-byte weight block
+    static constexpr int W_BLOCK = BN * 64;
+    static constexpr int W_LOADS = W_BLOCK / 16;             // 16-byte copies per weight block
+    static constexpr int S_GPB = 8;                          // scale groups per scale block
+    static constexpr int S_BLOCK = BN * 32;                  // two aligned 16-byte windows per row
+    static constexpr int S_LOADS = S_BLOCK / 16;
+    static_assert(MB >= 1 && NB >= 1, "wave tile too small");
+    static_assert(X_TILE % (16 * THREADS) == 0, "X tile is not a whole number of copies");
+    static_assert(W_LOADS % 64 == 0 && S_LOADS % 64 == 0, "blocks are whole waves of copies");
+};
+
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(GemmProblem p, int tiles_m,
+                                                                                int tiles_n) {
+    using C = Cfg<BITS, G, BM, BN, WAVES_M, WAVES_N>;
+    // Separate static buffers (not one array indexed by parity): the compiler can then see
+    // that reads of one buffer do not depend on copies still landing in the other.
+    __shared__ __attribute__((aligned(16))) unsigned char xa0[C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char xa1[C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char wk0[C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char wk1[C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk0[C::S_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk1[C::S_BLOCK];
 
     const int M = p.M, N = p.N, K = p.K;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
     const int half = lane >> 5, col = lane & 31;
 
@@ -68,59 +113,74 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmProblem p, 
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
 
     const int kgroups = K / G;
-    const int ksteps = (K + C::KS - 1) / C::KS;
-    const int words_per_row = K * BITS / 32;
+    const int ksub = K / C::SUBG;
+    const int ksteps = (K + KS - 1) / KS;
+    const uint32_t w_row_bytes = uint32_t(K) * BITS / 8;
+    const uint32_t s_row_bytes = uint32_t(kgroups) * 2u;
 
-    // ---- X tile loader: thread t handles 16-byte chunk t + i*kThreads of the tile ----
-    auto issue_x_loads = [&](int step, int buf) {
-        const int k0 = step * C::KS;
+    // ---- X: thread copies a fixed chunk column of rows r_first + i * rows_per_copy ----
+    constexpr int kRowsPerCopy = C::THREADS / kChunksPerRow;
+    const int r_first = tid / kChunksPerRow;
+    const uint32_t x_voff = uint32_t(r_first) * uint32_t(K) * 2u +
+                            uint32_t((tid % kChunksPerRow) ^ lds_swizzle(r_first)) * 16u;
+    const uint32_t x_row_step = uint32_t(kRowsPerCopy) * uint32_t(K) * 2u;
+    const unsigned char* x_tile = reinterpret_cast<const unsigned char*>(p.X) + size_t(m0) * size_t(K) * 2;
+    const uint32_t x_tile_bytes = uint32_t(M - m0 < BM ? M - m0 : BM) * uint32_t(K) * 2u;
+    auto issue_x = [&](int step, unsigned char* buf) {
+        const uint32_t kb = uint32_t(step) * KS * 2u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(x_tile + kb, x_tile_bytes - kb);
 #pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int slot = i * kThreads + threadIdx.x;          // LDS chunk index
-            const int r = slot / C::CHUNKS_PER_ROW;
-            const int pc = slot % C::CHUNKS_PER_ROW;
-            const int c = pc ^ (r & 7);                            // logical chunk stored there
-            int gr = m0 + r;
-            gr = gr < M ? gr : M - 1;
-            int gk = k0 + c * 8;
-            gk = gk < K ? gk : K - 8;
-            const uint16_t* src = p.X + int64_t(gr) * K + gk;
-            // LDS destination of the wave: base + lane*16, contiguous per wave
-            unsigned char* dst = smem + buf * C::TILE_BYTES + (i * kThreads + wave * 64) * 16;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
+        for (int i = 0; i < C::X_LOADS; ++i)
+            dma16(rs, buf + (i * C::THREADS + wave_u * 64) * 16, x_voff + uint32_t(i) * x_row_step, 0);
     };
 
-    // ---- per-lane weight rows: column n of Y for each 32-col block of the wave ----
-    int wrow[C::NB];
+    // ---- packed weights: block b holds steps [b*W_SPB, (b+1)*W_SPB) of the tile's BN rows.
+    // Copy slot t (of W_LOADS) = row t/4, stored chunk t%4, which holds source chunk
+    // (t%4) ^ w_swz(row).  Rows past N re-read row N-1.
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(N) * w_row_bytes);
+    auto issue_w = [&](int block, unsigned char* buf) {
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-        int n = n0 + wn0 + nb * 32 + col;
-        wrow[nb] = n < N ? n : N - 1;
-    }
-
-    uint32_t wcur[C::NB][C::GPS][C::WPH], wnxt[C::NB][C::GPS][C::WPH];
-    uint16_t scur[C::NB][C::GPS], snxt[C::NB][C::GPS];
-
-    auto load_w = [&](int step, uint32_t (&wd)[C::NB][C::GPS][C::WPH], uint16_t (&sd)[C::NB][C::GPS]) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-            for (int q = 0; q < C::GPS; ++q) {
-                int grp = step * C::GPS + q;
-                grp = grp < kgroups ? grp : kgroups - 1;
-                const uint32_t* src = p.W + int64_t(wrow[nb]) * words_per_row;
-                if (C::HALF_WORD) {
-                    wd[nb][q][0] = src[grp];
-                } else {
-                    const int off = grp * (2 * C::WPH) + half * C::WPH;
-#pragma unroll
-                    for (int w = 0; w < C::WPH; ++w) wd[nb][q][w] = src[off + w];
-                }
-                sd[nb][q] = p.S[int64_t(wrow[nb]) * kgroups + grp];
+        for (int i = 0; i < (C::W_LOADS + C::THREADS - 1) / C::THREADS; ++i) {
+            const int slot0 = i * C::THREADS + wave_u * 64;  // first slot of this wave's copy
+            if (slot0 < C::W_LOADS) {
+                const int slot = slot0 + lane;
+                const int r = slot >> 2;
+                int n = n0 + r;
+                n = n < N ? n : N - 1;
+                const uint32_t voff = uint32_t(n) * w_row_bytes + uint32_t(((slot & 3) ^ w_swz(r)) * 16);
+                dma16(w_rs, buf + slot0 * 16, voff, __builtin_amdgcn_readfirstlane(block * 64));
             }
         }
     };
+
+    // ---- scales: block b holds groups [8b, 8b+8) of the tile's BN rows as two aligned
+    // 16-byte windows per row (32 bytes); the row's group 8b sits (row offset & 15) bytes in.
+    const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(p.S, uint32_t(N) * s_row_bytes);
+    auto issue_s = [&](int block, unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < (C::S_LOADS + C::THREADS - 1) / C::THREADS; ++i) {
+            const int slot0 = i * C::THREADS + wave_u * 64;
+            if (slot0 < C::S_LOADS) {
+                const int slot = slot0 + lane;
+                const int r = slot >> 1;
+                int n = n0 + r;
+                n = n < N ? n : N - 1;
+                const uint32_t start = uint32_t(n) * s_row_bytes + uint32_t(block) * 16u;
+                const uint32_t voff = (start & ~15u) + uint32_t(slot & 1) * 16u;
+                dma16(s_rs, buf + slot0 * 16, voff, 0);
+            }
+        }
+    };
+
+    // Per-lane byte offset of its NB weight rows' group 8b within a scale block.
+    int s_rd[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+        const int r = wn0 + nb * 32 + col;
+        int n = n0 + r;
+        n = n < N ? n : N - 1;
+        s_rd[nb] = r * 32 + int((uint32_t(n) * s_row_bytes) & 15u);
+    }
 
     f32x16_t acc[C::MB][C::NB];
 #pragma unroll
@@ -130,80 +190,140 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmProblem p, 
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-    issue_x_loads(0, 0);
-    load_w(0, wcur, scur);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
     const float code_scale = BITS == 2 ? 0.5f : -0.5f;  // operand holds 2c (ternary), -2c (binary)
 
-    for (int step = 0; step < ksteps; ++step) {
-        const int buf = step & 1;
-        const bool more = step + 1 < ksteps;
-        if (more) {
-            issue_x_loads(step + 1, buf ^ 1);
-            load_w(step + 1, wnxt, snxt);
-        }
-        const unsigned char* xt = smem + buf * C::TILE_BYTES;
-
+    // A step's packed words and scales are read from LDS into registers before any copy of
+    // the step is issued: the compiler cannot tell which of the two weight / scale buffers a
+    // step reads, and would otherwise wait for every copy in flight before these reads.
+    typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+    constexpr int kWordsPerLane = (C::SUBG / 2) * BITS / 32 > 0 ? (C::SUBG / 2) * BITS / 32 : 1;
+    struct Ops {
+        uint32_t w[C::GPS][C::NB][kWordsPerLane];
+        float sc[C::GPS][C::NB];
+    };
+    auto read_operands = [&](const unsigned char* wt, const unsigned char* st, int step, Ops& o) {
+        const int wj = step % C::W_SPB;  // step within the weight block
 #pragma unroll
         for (int q = 0; q < C::GPS; ++q) {
-            if (step * C::GPS + q >= kgroups) break;  // K tail (g = 32 with K % 64 == 32)
+            const int grp = (step * KS + q * C::SUBG) / G;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int r = wn0 + nb * 32 + col;
+                o.sc[q][nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + (grp & 7) * 2)) *
+                              code_scale;
+                // this lane's codes: sub-group q of the step, half `half` -> SUBG/2 codes
+                const int code0 = q * C::SUBG + half * (C::SUBG / 2);       // within the step
+                const int byte0 = wj * C::W_STEP_BYTES + code0 * BITS / 8;  // within the block row
+                const int chunk = byte0 >> 4, inb = byte0 & 15;
+                const unsigned char* src = wt + r * 64 + ((chunk ^ w_swz(r)) << 4) + inb;
+                if constexpr (kWordsPerLane == 2) {
+                    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
+                    o.w[q][nb][0] = v[0];
+                    o.w[q][nb][1] = v[1];
+                } else if constexpr ((C::SUBG / 2) * BITS >= 32) {
+                    o.w[q][nb][0] = *reinterpret_cast<const uint32_t*>(src);
+                } else {  // binary g = 32: 16 codes = half of an aligned word
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(src - (inb & 3));
+                    o.w[q][nb][0] = w >> ((inb & 2) * 8);
+                }
+            }
+        }
+    };
 
-            // Expand this group's codes: bfr[nb][j] = operand of MFMA chunk j.
+    auto compute = [&](const unsigned char* xt, const Ops& o, int step) {
+#pragma unroll
+        for (int q = 0; q < C::GPS; ++q) {
+            if (C::GPS > 1 && step * C::GPS + q >= ksub) break;  // K tail (g = 32, K % 64 == 32)
             u32x4_t bfr[C::NB][C::CHUNKS];
             float sc[C::NB];
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
+                sc[nb] = o.sc[q][nb];
                 uint32_t d[C::CHUNKS * 4];
-                if (BITS == 2) {
+                if constexpr (BITS == 2) {
 #pragma unroll
-                    for (int w = 0; w < C::WPH; ++w) expand_ternary_word(wcur[nb][q][w], d + 8 * w);
-                } else if (C::HALF_WORD) {
-                    expand_binary_word<8>(wcur[nb][q][0] >> (16 * half), d);
+                    for (int w = 0; w < kWordsPerLane; ++w) expand_ternary_word(o.w[q][nb][w], d + 8 * w);
+                } else if constexpr (C::SUBG == 64) {
+                    expand_binary_word<16>(o.w[q][nb][0], d);
                 } else {
-#pragma unroll
-                    for (int w = 0; w < C::WPH; ++w) expand_binary_word<16>(wcur[nb][q][w], d + 16 * w);
+                    expand_binary_word<8>(o.w[q][nb][0], d);
                 }
 #pragma unroll
                 for (int j = 0; j < C::CHUNKS; ++j)
                     bfr[nb][j] = u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
-                sc[nb] = half_bits_to_float(scur[nb][q]) * code_scale;
             }
 
+            // Blocks b = mb*NB + nb in order; the MFMA chain of block b is issued before the
+            // scale FMAs of block b-1, which use the other partial-sum registers.
+            f32x16_t tmp[2];
+            bf16x8_t afr[C::CHUNKS];
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) {
-                const int row = wm0 + mb * 32 + col;
-                bf16x8_t afr[C::CHUNKS];
+            for (int b = 0; b <= C::MB * C::NB; ++b) {
+                if (b < C::MB * C::NB) {
+                    const int mb = b / C::NB, nb = b % C::NB;
+                    if (nb == 0) {
+                        const int row = wm0 + mb * 32 + col;
 #pragma unroll
-                for (int j = 0; j < C::CHUNKS; ++j) {
-                    const int chunk = (q * G + half * (G / 2)) / 8 + j;
-                    afr[j] = *reinterpret_cast<const bf16x8_t*>(xt + lds_offset(row, chunk, C::ROW_BYTES));
-                }
-#pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    f32x16_t tmp = {};
+                        for (int j = 0; j < C::CHUNKS; ++j)
+                            afr[j] = *reinterpret_cast<const bf16x8_t*>(
+                                xt + x_off(row, (q * C::SUBG + half * (C::SUBG / 2)) / 8 + j));
+                    }
+                    f32x16_t t = {};
 #pragma unroll
                     for (int j = 0; j < C::CHUNKS; ++j)
-                        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            afr[j], __builtin_bit_cast(bf16x8_t, bfr[nb][j]), tmp, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[j], __builtin_bit_cast(bf16x8_t, bfr[nb][j]),
+                                                                    t, 0, 0, 0);
+                    tmp[b & 1] = t;
+                }
+                if (b > 0) {
+                    const int pb = b - 1, mb = pb / C::NB, nb = pb % C::NB;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[mb][nb][i] = __builtin_fmaf(sc[nb], tmp[i], acc[mb][nb][i]);
+                    for (int i = 0; i < 16; ++i)
+                        acc[mb][nb][i] = __builtin_fmaf(sc[nb], tmp[pb & 1][i], acc[mb][nb][i]);
                 }
             }
         }
+    };
 
-        if (more) {
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < C::GPS; ++q) {
-                    scur[nb][q] = snxt[nb][q];
-#pragma unroll
-                    for (int w = 0; w < C::WPH; ++w) wcur[nb][q][w] = wnxt[nb][q][w];
-                }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Block bookkeeping: the weight block of step s is s / W_SPB, its scale block group / 8.
+    auto w_buf = [&](int step) -> unsigned char* { return ((step / C::W_SPB) & 1) ? wk1 : wk0; };
+    auto s_block = [&](int step) { return (step * KS / G) / C::S_GPB; };
+    auto s_buf = [&](int step) -> unsigned char* { return (s_block(step) & 1) ? sk1 : sk0; };
+    const int w_blocks = (ksteps + C::W_SPB - 1) / C::W_SPB;
+    const int s_blocks = (kgroups + C::S_GPB - 1) / C::S_GPB;
+
+    // During step s: X of step s+1, and -- on the first step of a weight or scale block --
+    // the whole next block into the other buffer (after this step's operands were read).
+    auto prefetch_x = [&](int step, unsigned char* xbuf) {
+        if (step + 1 < ksteps) issue_x(step + 1, xbuf);
+    };
+    auto prefetch_blocks = [&](int step) {
+        if (step % C::W_SPB == 0 && step / C::W_SPB + 1 < w_blocks)
+            issue_w(step / C::W_SPB + 1, w_buf(step + C::W_SPB));
+        const int sb = s_block(step);
+        if ((step == 0 || s_block(step - 1) != sb) && sb + 1 < s_blocks) issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+    };
+
+    issue_x(0, xa0);
+    issue_w(0, wk0);
+    issue_s(0, sk0);
+    wait_vmcnt0();
+    __syncthreads();
+
+    Ops ops;
+    for (int step = 0; step < ksteps; step += 2) {
+        read_operands(w_buf(step), s_buf(step), step, ops);
+        prefetch_x(step, xa1);
+        prefetch_blocks(step);
+        compute(xa0, ops, step);
+        wait_vmcnt0();
+        __syncthreads();
+        if (step + 1 >= ksteps) break;
+        read_operands(w_buf(step + 1), s_buf(step + 1), step + 1, ops);
+        prefetch_x(step + 1, xa0);
+        prefetch_blocks(step + 1);
+        compute(xa1, ops, step + 1);
+        wait_vmcnt0();
         __syncthreads();
     }
 
@@ -223,30 +343,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmProblem p, 
     }
 }
 
-template <int BITS, int G, int BM, int BN, int WAVES_M>
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
-    using C = TileCfg<BITS, G, BM, BN, WAVES_M>;
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = (p.N + BN - 1) / BN;
-    const size_t lds = 2 * size_t(C::TILE_BYTES);
-    auto kern = gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M>;
-    static bool attr_set = false;  // per instantiation; idempotent if raced
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), lds, stream, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N>), dim3(tiles_m * tiles_n),
+                       dim3(64 * WAVES_M * WAVES_N), 0, stream, p, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 template <int BITS, int G>
 hipError_t launch_bits_g(const GemmProblem& p, int variant, hipStream_t stream) {
     switch (variant) {
-        case TILE_256x128: return launch_cfg<BITS, G, 256, 128, 2>(p, stream);
-        case TILE_128x128: return launch_cfg<BITS, G, 128, 128, 2>(p, stream);
-        default:           return launch_cfg<BITS, G, 64, 128, 2>(p, stream);
+        case TILE_256x256: return launch_cfg<BITS, G, 256, 256, 2, 4>(p, stream);
+        case TILE_128x256: return launch_cfg<BITS, G, 128, 256, 1, 4>(p, stream);
+        default:           return launch_cfg<BITS, G, 64, 256, 1, 4>(p, stream);
     }
 }
 
@@ -254,9 +365,9 @@ hipError_t launch_bits_g(const GemmProblem& p, int variant, hipStream_t stream) 
 
 int pick_tile_variant(int64_t M, int64_t N, int64_t K) {
     (void)N; (void)K;
-    if (M >= 1024) return TILE_256x128;
-    if (M >= 256) return TILE_128x128;
-    return TILE_64x128;
+    if (M >= 1024) return TILE_256x256;
+    if (M >= 256) return TILE_128x256;
+    return TILE_64x256;
 }
 
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream) {

@@ -65,6 +65,14 @@ __device__ __forceinline__ void expand_binary_word(uint32_t w, uint32_t out[NOUT
     }
 }
 
+// LDS tiles are stored as rows of 128-byte (or 256-byte) lines of 16-byte chunks; chunk c of
+// row r lives at chunk position c ^ lds_swizzle(r).  gfx950's LDS serves a 128-bit read for
+// 16 lanes per cycle across 64 four-byte banks, i.e. 16 distinct 16-byte bank groups.  The
+// MFMA operand reads have 16 lanes on 16 consecutive rows at the same logical chunk; a
+// 128-byte row covers half the banks, so even and odd rows already differ in the upper
+// half and the XOR only has to separate the 8 rows of each parity: (r >> 1) & 7.
+__device__ __forceinline__ int lds_swizzle(int row) { return (row >> 1) & 7; }
+
 // fp16 bits -> fp32 (exact).
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));

@@ -19,8 +19,8 @@ hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, i
 hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
                          hipStream_t stream);
 
-// Large-M tile kernel (MFMA, LDS-staged X).  `variant` selects the tile shape.
-enum TileVariant { TILE_256x128 = 0, TILE_128x128 = 1, TILE_64x128 = 2 };
+// Tiled MFMA kernel (LDS-staged X, packed weights and scales).  `variant` selects the tile.
+enum TileVariant { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2 };
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.

@@ -103,13 +103,14 @@ def test_gemm_small(M, N, K, g, bits):
 
 
 @pytest.mark.parametrize("variant", ["tile256", "tile128", "tile64", "skinny"])
-@pytest.mark.parametrize("M", [16, 300])
+@pytest.mark.parametrize("M", [16, 300, 600])
 def test_every_variant(variant, M, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
     for bits in (2, 1):
-        inp = _inputs(M, 400, 320, 64, bits)
-        y, _ = run_gemm(inp, 64, bits)
-        _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, 64), f"{variant} M={M} b{bits}")
+        for g, K in ((64, 320), (32, 352), (128, 384)):
+            inp = _inputs(M, 400, K, g, bits)
+            y, _ = run_gemm(inp, g, bits)
+            _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{variant} M={M} g{g} b{bits}")
 
 
 def test_empty_and_k0():
