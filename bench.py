@@ -29,6 +29,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+KERNEL_SOURCES = ["binary_bit_gemm_amd/csrc/gemm_tiled.hip", "binary_bit_gemm_amd/csrc/lowbit_device.h"]
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when there is none
+    for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
 PEAK_HBM_GBS = 8000.0
 METRIC = "lowbit GEMM TFLOP/s and % of bf16 MFMA peak (M=4608, ternary g=64)"
 
@@ -42,7 +66,10 @@ def parse():
                     choices=["res1024", "res512", "res512_binary", "sweep", "skinny"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of X in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of X in the CPU oracle sample (0 = all rows of the workload)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -102,7 +129,7 @@ def cpu_baseline(probs, rows, seed):
     flops = 0
     elapsed = 0.0
     for (N, K, bits, g), p in seen.items():
-        m = min(rows, p.M)
+        m = p.M if rows <= 0 else min(rows, p.M)
         q = W.Problem(p.name, m, N, K, bits, g, p.config_id, p.tensor_id)
         inp = W.make_inputs(q, seed)
         words, _ = oracle.pack(inp.codes, bits)
@@ -111,7 +138,8 @@ def cpu_baseline(probs, rows, seed):
         elapsed += time.perf_counter() - t0
         flops += 2 * m * N * K
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} rows of X for each of the {len(seen)} distinct (N, K) shapes; "
+            "sample": (f"all {probs[0].M}" if rows <= 0 else f"first {rows}") +
+                      f" rows of X for each of the {len(seen)} distinct (N, K) shapes; "
                       f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s"}
 
 
@@ -123,6 +151,15 @@ def main():
         sys.exit(2)
     import torch
     import binary_bit_gemm_amd as lb
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2}))
+        return
 
     probs = problems_for(a.workload)
     bufs = make_device_inputs(probs, a.seed)
@@ -168,12 +205,14 @@ def main():
         metric, value, unit = "lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)", \
             bytes_step / (elapsed / a.steps) / 1e9, "GB/s"
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(a.workload),
+                "algorithmic_bytes_per_launch": bytes_step // len(probs)}
     else:
         metric = METRIC if a.workload == "res1024" else METRIC.replace("(M=4608, ternary g=64)", f"({a.workload})")
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.workload),
+                "algorithmic_bytes_per_launch": bytes_step // len(probs)}
     variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
     out = {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": a.steps,

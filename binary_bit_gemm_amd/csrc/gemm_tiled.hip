@@ -58,12 +58,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_
 
 __device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
 
-// Packed-weight block: 64 bytes per row = four 16-byte chunks; chunk c of row r is stored at
-// position c ^ ((r >> 2) & 3) so that 16 consecutive rows reading the same chunk hit 16
-// different bank groups.
-__device__ __forceinline__ int w_swz(int row) { return (row >> 2) & 3; }
+// Packed-weight block: WB (32 or 64) bytes per row = WB/16 chunks of 16 bytes; chunk c of row
+// r is stored at position c ^ w_swz(r) so that 16 consecutive rows reading the same chunk
+// hit 16 different bank groups.
+template <int WB>
+__device__ __forceinline__ int w_swz(int row) { return WB == 64 ? (row >> 2) & 3 : (row >> 3) & 1; }
 
-template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
 struct Cfg {
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
@@ -75,8 +76,9 @@ struct Cfg {
     static constexpr int X_TILE = BM * kRowBytes;
     static constexpr int X_LOADS = X_TILE / (16 * THREADS);  // 16-byte copies per thread per step
     static constexpr int W_STEP_BYTES = KS * BITS / 8;       // packed bytes of one row per step
-    static constexpr int W_SPB = 64 / W_STEP_BYTES;          // steps per 64-byte weight block
-    static constexpr int W_BLOCK = BN * 64;
+    static constexpr int W_SPB = WB / W_STEP_BYTES;          // steps per WB-byte weight block
+    static constexpr int W_CPR = WB / 16;                    // 16-byte chunks per row of a block
+    static constexpr int W_BLOCK = BN * WB;
     static constexpr int W_LOADS = W_BLOCK / 16;             // 16-byte copies per weight block
     static constexpr int S_GPB = 8;                          // scale groups per scale block
     static constexpr int S_BLOCK = BN * 32;                  // two aligned 16-byte windows per row
@@ -86,10 +88,10 @@ struct Cfg {
     static_assert(W_LOADS % 64 == 0 && S_LOADS % 64 == 0, "blocks are whole waves of copies");
 };
 
-template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(GemmProblem p, int tiles_m,
                                                                                 int tiles_n) {
-    using C = Cfg<BITS, G, BM, BN, WAVES_M, WAVES_N>;
+    using C = Cfg<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>;
     // Separate static buffers (not one array indexed by parity): the compiler can then see
     // that reads of one buffer do not depend on copies still landing in the other.
     __shared__ __attribute__((aligned(16))) unsigned char xa0[C::X_TILE];
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
     };
 
     // ---- packed weights: block b holds steps [b*W_SPB, (b+1)*W_SPB) of the tile's BN rows.
-    // Copy slot t (of W_LOADS) = row t/4, stored chunk t%4, which holds source chunk
-    // (t%4) ^ w_swz(row).  Rows past N re-read row N-1.
+    // Copy slot t (of W_LOADS) = row t/W_CPR, stored chunk t%W_CPR, which holds source chunk
+    // (t%W_CPR) ^ w_swz(row).  Rows past N re-read row N-1.
     const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(N) * w_row_bytes);
     auto issue_w = [&](int block, unsigned char* buf) {
 #pragma unroll
@@ -144,11 +146,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
             const int slot0 = i * C::THREADS + wave_u * 64;  // first slot of this wave's copy
             if (slot0 < C::W_LOADS) {
                 const int slot = slot0 + lane;
-                const int r = slot >> 2;
+                const int r = slot / C::W_CPR;
                 int n = n0 + r;
                 n = n < N ? n : N - 1;
-                const uint32_t voff = uint32_t(n) * w_row_bytes + uint32_t(((slot & 3) ^ w_swz(r)) * 16);
-                dma16(w_rs, buf + slot0 * 16, voff, __builtin_amdgcn_readfirstlane(block * 64));
+                const uint32_t voff = uint32_t(n) * w_row_bytes + uint32_t(((slot % C::W_CPR) ^ w_swz<WB>(r)) * 16);
+                dma16(w_rs, buf + slot0 * 16, voff, __builtin_amdgcn_readfirstlane(block * WB));
             }
         }
     };
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
                 const int code0 = q * C::SUBG + half * (C::SUBG / 2);       // within the step
                 const int byte0 = wj * C::W_STEP_BYTES + code0 * BITS / 8;  // within the block row
                 const int chunk = byte0 >> 4, inb = byte0 & 15;
-                const unsigned char* src = wt + r * 64 + ((chunk ^ w_swz(r)) << 4) + inb;
+                const unsigned char* src = wt + r * WB + ((chunk ^ w_swz<WB>(r)) << 4) + inb;
                 if constexpr (kWordsPerLane == 2) {
                     const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
                     o.w[q][nb][0] = v[0];
@@ -343,21 +345,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
     }
 }
 
-template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>), dim3(tiles_m * tiles_n),
                        dim3(64 * WAVES_M * WAVES_N), 0, stream, p, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 template <int BITS, int G>
 hipError_t launch_bits_g(const GemmProblem& p, int variant, hipStream_t stream) {
+    // LDS: 256x128 = 80 KB and 128x256 = 72 KB (two workgroups per CU); 256x256 = 112 KB.
     switch (variant) {
-        case TILE_256x256: return launch_cfg<BITS, G, 256, 256, 2, 4>(p, stream);
-        case TILE_128x256: return launch_cfg<BITS, G, 128, 256, 1, 4>(p, stream);
-        default:           return launch_cfg<BITS, G, 64, 256, 1, 4>(p, stream);
+        case TILE_256x128: return launch_cfg<BITS, G, 256, 128, 2, 2, 32>(p, stream);
+        case TILE_256x256: return launch_cfg<BITS, G, 256, 256, 2, 4, 64>(p, stream);
+        case TILE_128x256: return launch_cfg<BITS, G, 128, 256, 1, 4, 32>(p, stream);
+        default:           return launch_cfg<BITS, G, 64, 256, 1, 4, 32>(p, stream);
     }
 }
 

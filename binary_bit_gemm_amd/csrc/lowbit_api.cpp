@@ -47,12 +47,13 @@ int device_check() {
     return r == 1 ? LOWBIT_OK : LOWBIT_E_UNSUPPORTED;
 }
 
-// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | tile256 | tile128 | tile64
+// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | tile256 | tile256w | tile128 | tile64
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
     if (std::strcmp(v, "skinny") == 0) return 100;
-    if (std::strcmp(v, "tile256") == 0) return lowbit::TILE_256x256;
+    if (std::strcmp(v, "tile256") == 0) return lowbit::TILE_256x128;
+    if (std::strcmp(v, "tile256w") == 0) return lowbit::TILE_256x256;
     if (std::strcmp(v, "tile128") == 0) return lowbit::TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return lowbit::TILE_64x256;
     return -1;
@@ -141,6 +142,7 @@ const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits
     (void)g; (void)bits;
     switch (choose_variant(M, N, K)) {
         case 100: return "skinny";
+        case lowbit::TILE_256x128: return "tile256x128";
         case lowbit::TILE_256x256: return "tile256x256";
         case lowbit::TILE_128x256: return "tile128x256";
         default: return "tile64x256";

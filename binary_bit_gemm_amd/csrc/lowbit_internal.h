@@ -20,7 +20,7 @@ hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K,
                          hipStream_t stream);
 
 // Tiled MFMA kernel (LDS-staged X, packed weights and scales).  `variant` selects the tile.
-enum TileVariant { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2 };
+enum TileVariant { TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3 };
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
