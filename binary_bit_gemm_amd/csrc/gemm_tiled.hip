@@ -32,29 +32,11 @@
 namespace lowbit {
 namespace {
 
-constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, gfx9 family
 constexpr int KS = 64;                    // K elements per step
 constexpr int kRowBytes = KS * 2;         // one bf16 row of an X tile
 constexpr int kChunksPerRow = KS / 8;     // 16-byte chunks per X row
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Buffer resource with its fields forced into scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
-    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, int(n),
-                                             kBufferFlags);
-}
-
-// 16-byte direct-to-LDS copy; the wave's 64 lanes land at consecutive 16-byte slots from
-// lds_wave_base.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
-                                            soff, 0, 0);
-}
 
 __device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
 

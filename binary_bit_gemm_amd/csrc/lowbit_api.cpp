@@ -59,11 +59,11 @@ int forced_variant() {
     return -1;
 }
 
-int choose_variant(int64_t M, int64_t N, int64_t K) {
+int choose_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     const int f = forced_variant();
-    if (f == 100 && M <= 32) return 100;
+    if (f == 100 && lowbit::use_skinny(M, N, K, g, bits)) return 100;
     if (f >= 0 && f != 100) return f;
-    if (lowbit::use_skinny(M, N, K)) return 100;
+    if (lowbit::use_skinny(M, N, K, g, bits)) return 100;
     return lowbit::pick_tile_variant(M, N, K);
 }
 
@@ -80,7 +80,7 @@ int launch_one(const lowbit::GemmProblem& p, int g, int bits, hipStream_t stream
         hipLaunchKernelGGL(zero_fill_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, p.Y, n);
         e = hipGetLastError();
     } else {
-        const int v = choose_variant(p.M, p.N, p.K);
+        const int v = choose_variant(p.M, p.N, p.K, g, bits);
         e = v == 100 ? lowbit::launch_gemm_skinny(p, g, bits, stream)
                      : lowbit::launch_gemm_tiled(p, g, bits, v, stream);
     }
@@ -139,8 +139,7 @@ int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, cons
 }
 
 const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
-    (void)g; (void)bits;
-    switch (choose_variant(M, N, K)) {
+    switch (choose_variant(M, N, K, g, bits)) {
         case 100: return "skinny";
         case lowbit::TILE_256x128: return "tile256x128";
         case lowbit::TILE_256x256: return "tile256x256";

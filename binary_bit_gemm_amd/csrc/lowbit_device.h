@@ -93,4 +93,22 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
     return x * base + (x < extra ? x : extra) + slot;
 }
 
+// Raw buffer resource (gfx9 family flags) with its fields forced into scalar registers.  Loads
+// through it at offsets at or past `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, int(n),
+                                             0x00020000);
+}
+
+// 16-byte direct-to-LDS copy: lane i's 16 bytes (at voff + soff in the buffer) land at
+// lds_wave_base + 16 * i.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                            soff, 0, 0);
+}
+
 }  // namespace lowbit

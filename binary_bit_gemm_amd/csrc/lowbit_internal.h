@@ -24,13 +24,17 @@ enum TileVariant { TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
+// Shapes it does not cover (M > 32, K not a whole number of 64-byte row steps, or a
+// (g, bits) whose scale group is smaller than the kernel's 16-byte chunk) go to the 64 x 256
+// tile.
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream);
+bool skinny_supported(int g, int bits);
 
 // Grouped launch: several problems of the same (g, bits) in one persistent launch.
 hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int bits,
                                hipStream_t stream);
 
 int pick_tile_variant(int64_t M, int64_t N, int64_t K);
-bool use_skinny(int64_t M, int64_t N, int64_t K);
+bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit

@@ -88,5 +88,22 @@ def test_gemm_rejects_before_touching_the_device():
 
 
 def test_variant_choice():
-    assert lb.variant(4608, 18432, 3072).startswith("tile")
-    assert lb.variant(64, 256, 256) in ("tile64x256", "skinny")
+    assert lb.variant(4608, 18432, 3072) == "tile256x256"
+    assert lb.variant(1536, 3072, 3072) == "tile256x256"
+    assert lb.variant(512, 3072, 3072) == "tile128x256"
+    assert lb.variant(64, 256, 256) == "tile64x256"
+
+
+def test_skinny_variant_choice():
+    """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) when a 16-byte chunk of
+    a packed row lies in one scale group and K is a whole number of 64-byte row steps."""
+    assert lb.variant(16, 3072, 3072, 64, 2) == "skinny"
+    assert lb.variant(1, 27648, 3072, 128, 2) == "skinny"
+    assert lb.variant(32, 3072, 12288, 64, 2) == "skinny"
+    assert lb.variant(33, 3072, 3072, 64, 2) == "tile64x256"
+    assert lb.variant(16, 3072, 3072, 32, 2) == "tile64x256"     # group of 32 < chunk of 64
+    assert lb.variant(16, 3072, 320, 64, 2) == "tile64x256"      # K % 256 != 0
+    assert lb.variant(16, 3072, 3072, 128, 1) == "skinny"
+    assert lb.variant(16, 3072, 3072, 64, 1) == "tile64x256"     # binary chunk is 128 codes
+    assert lb.variant(16, 3072, 2816, 128, 1) == "tile64x256"    # K % 512 != 0
+    assert lb.variant(17, 3072, 3072, 128, 1) == "tile64x256"
