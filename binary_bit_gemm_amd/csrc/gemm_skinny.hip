@@ -52,7 +52,7 @@ __device__ __forceinline__ void transpose_words(u32x4_t& w) {
 }
 
 template <int BITS, int G, int MB, int NCB, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(GemmProblem p) {
+__global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup grp) {
     using F = SkinnyFmt<BITS>;
     constexpr int GPS = F::STEP / G;     // scale groups per step
     constexpr int CPG = G / F::CHUNK;    // chunks per scale group (1 or 2)
@@ -76,11 +76,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(GemmProblem 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int q = lane >> 4, n = lane & 15;
+    int pi = 0;
+    while (pi + 1 < grp.count && int(blockIdx.x) >= grp.tile_end[pi]) ++pi;
+    const GemmProblem p = grp.p[pi];
+    const int stripe = int(blockIdx.x) - (pi > 0 ? grp.tile_end[pi - 1] : 0);
     const int M = p.M, N = p.N, K = p.K;
 
     // The host guarantees N % (16 * NCB) == 0 and K % STEP == 0 (whole steps, so every
     // row's scales of a step are one aligned 4- or 8-byte piece).
-    const int n0 = blockIdx.x * (16 * NCB);
+    const int n0 = stripe * (16 * NCB);
     const uint32_t row_bytes = uint32_t(K) * BITS / 8;
     const int kgroups = K / G;
     const uint32_t s_row_bytes = uint32_t(kgroups) * 2u;
@@ -255,10 +259,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(GemmProblem 
 }
 
 template <int BITS, int G, int MB, int NCB>
-hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
+hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
     constexpr int WAVES = 4;
-    hipLaunchKernelGGL((gemm_skinny_kernel<BITS, G, MB, NCB, WAVES>), dim3(p.N / (16 * NCB)), dim3(64 * WAVES), 0,
-                       stream, p);
+    ProblemGroup grp{};
+    int total = 0;
+    for (int i = 0; i < count; ++i) {
+        grp.p[i] = probs[i];
+        total += probs[i].N / (16 * NCB);
+        grp.tile_end[i] = total;
+    }
+    grp.count = count;
+    hipLaunchKernelGGL((gemm_skinny_kernel<BITS, G, MB, NCB, WAVES>), dim3(total), dim3(64 * WAVES), 0, stream, grp);
     return hipGetLastError();
 }
 
@@ -266,33 +277,49 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 // ternary codes, two for binary codes (twice the activation operands per step), one for two
 // row blocks.
 template <int BITS, int G, int MB>
-hipError_t launch_mb(const GemmProblem& p, int ncb, hipStream_t stream) {
+hipError_t launch_mb(const GemmProblem* probs, int count, int ncb, hipStream_t stream) {
     if constexpr (MB == 1 && BITS == 2) {
-        if (ncb >= 4) return launch_cfg<BITS, G, MB, 4>(p, stream);
+        if (ncb >= 4) return launch_cfg<BITS, G, MB, 4>(probs, count, stream);
     }
     if constexpr (MB == 1) {
-        if (ncb >= 2) return launch_cfg<BITS, G, MB, 2>(p, stream);
+        if (ncb >= 2) return launch_cfg<BITS, G, MB, 2>(probs, count, stream);
     }
-    return launch_cfg<BITS, G, MB, 1>(p, stream);
+    return launch_cfg<BITS, G, MB, 1>(probs, count, stream);
 }
 
 template <int BITS, int G>
-hipError_t launch_bits_g(const GemmProblem& p, int ncb, hipStream_t stream) {
+hipError_t launch_bits_g(const GemmProblem* probs, int count, int max_m, int ncb, hipStream_t stream) {
     if constexpr (BITS == 1) {
-        return launch_mb<BITS, G, 1>(p, ncb, stream);
+        return launch_mb<BITS, G, 1>(probs, count, ncb, stream);
     } else {
-        return p.M <= 16 ? launch_mb<BITS, G, 1>(p, ncb, stream) : launch_mb<BITS, G, 2>(p, ncb, stream);
+        return max_m <= 16 ? launch_mb<BITS, G, 1>(probs, count, ncb, stream)
+                           : launch_mb<BITS, G, 2>(probs, count, ncb, stream);
     }
 }
 
-// Column blocks per workgroup: the widest stripe (dividing N / 16) that still gives every
-// compute unit about two workgroups -- X is re-read from L2 once per workgroup, so wider
-// stripes read less of it.
-int pick_ncb(int64_t N) {
-    const int64_t blocks = N / 16;
-    if (blocks % 4 == 0 && blocks >= 4 * 512) return 4;
-    if (blocks % 2 == 0 && blocks >= 2 * 384) return 2;
-    return 1;
+// Column blocks per workgroup: the widest stripe (dividing every N / 16) that still gives
+// every compute unit about two workgroups -- X is re-read from L2 once per workgroup, so
+// wider stripes read less of it.
+int pick_ncb(const GemmProblem* probs, int count) {
+    int64_t blocks = 0;
+    bool div4 = true, div2 = true;
+    for (int i = 0; i < count; ++i) {
+        const int64_t b = probs[i].N / 16;
+        blocks += b;
+        div4 = div4 && b % 4 == 0;
+        div2 = div2 && b % 2 == 0;
+    }
+    int ncb = 1;
+    if (div4 && blocks >= 4 * 512) {
+        ncb = 4;
+    } else if (div2 && blocks >= 2 * 384) {
+        ncb = 2;
+    }
+    if (const char* e = std::getenv("LOWBIT_SKINNY_NCB")) {
+        const int v = std::atoi(e);
+        if ((v == 1) || (v == 2 && div2) || (v == 4 && div4)) ncb = v;
+    }
+    return ncb;
 }
 
 }  // namespace
@@ -305,16 +332,20 @@ bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits) {
     return M <= (bits == 2 ? 32 : 16) && skinny_supported(g, bits) && K % step == 0;
 }
 
+hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
+    int max_m = 0;
+    for (int i = 0; i < count; ++i) max_m = probs[i].M > max_m ? probs[i].M : max_m;
+    const int ncb = pick_ncb(probs, count);
+    if (bits == 2) {
+        return g == 64 ? launch_bits_g<2, 64>(probs, count, max_m, ncb, stream)
+                       : launch_bits_g<2, 128>(probs, count, max_m, ncb, stream);
+    }
+    return launch_bits_g<1, 128>(probs, count, max_m, ncb, stream);
+}
+
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream) {
     if (!use_skinny(p.M, p.N, p.K, g, bits)) return launch_gemm_tiled(p, g, bits, TILE_64x256, stream);
-    int ncb = pick_ncb(p.N);
-    if (const char* e = std::getenv("LOWBIT_SKINNY_NCB")) {
-        const int v = std::atoi(e);
-        const int64_t blocks = p.N / 16;
-        if ((v == 1 || v == 2 || v == 4) && blocks % v == 0) ncb = v;
-    }
-    if (bits == 2) return g == 64 ? launch_bits_g<2, 64>(p, ncb, stream) : launch_bits_g<2, 128>(p, ncb, stream);
-    return launch_bits_g<1, 128>(p, ncb, stream);
+    return launch_gemm_skinny_group(&p, 1, g, bits, stream);
 }
 
 }  // namespace lowbit

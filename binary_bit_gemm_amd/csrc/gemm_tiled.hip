@@ -71,8 +71,7 @@ struct Cfg {
 };
 
 template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(GemmProblem p, int tiles_m,
-                                                                                int tiles_n) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(ProblemGroup grp) {
     using C = Cfg<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>;
     // Separate static buffers (not one array indexed by parity): the compiler can then see
     // that reads of one buffer do not depend on copies still landing in the other.
@@ -83,7 +82,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
     __shared__ __attribute__((aligned(16))) unsigned char sk0[C::S_BLOCK];
     __shared__ __attribute__((aligned(16))) unsigned char sk1[C::S_BLOCK];
 
+    // Workgroup -> (problem, tile); the tiles one XCD runs are contiguous in the group's
+    // tile order.
+    const int t = xcd_remap(blockIdx.x, grp.tile_end[grp.count - 1]);
+    int pi = 0;
+    while (pi + 1 < grp.count && t >= grp.tile_end[pi]) ++pi;
+    const GemmProblem p = grp.p[pi];
+    const int tile = t - (pi > 0 ? grp.tile_end[pi - 1] : 0);
     const int M = p.M, N = p.N, K = p.K;
+    const int tiles_n = (N + BN - 1) / BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -91,7 +98,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
     const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
     const int half = lane >> 5, col = lane & 31;
 
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile / tiles_n, tn = tile % tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
@@ -328,22 +334,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(G
 }
 
 template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
-hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
-    const int tiles_m = (p.M + BM - 1) / BM;
-    const int tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>), dim3(tiles_m * tiles_n),
-                       dim3(64 * WAVES_M * WAVES_N), 0, stream, p, tiles_m, tiles_n);
+hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
+    ProblemGroup grp{};
+    int total = 0;
+    for (int i = 0; i < count; ++i) {
+        grp.p[i] = probs[i];
+        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + BN - 1) / BN);
+        grp.tile_end[i] = total;
+    }
+    grp.count = count;
+    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>), dim3(total),
+                       dim3(64 * WAVES_M * WAVES_N), 0, stream, grp);
     return hipGetLastError();
 }
 
 template <int BITS, int G>
-hipError_t launch_bits_g(const GemmProblem& p, int variant, hipStream_t stream) {
+hipError_t launch_bits_g(const GemmProblem* probs, int count, int variant, hipStream_t stream) {
     // LDS: 256x128 = 80 KB and 128x256 = 72 KB (two workgroups per CU); 256x256 = 112 KB.
     switch (variant) {
-        case TILE_256x128: return launch_cfg<BITS, G, 256, 128, 2, 2, 32>(p, stream);
-        case TILE_256x256: return launch_cfg<BITS, G, 256, 256, 2, 4, 64>(p, stream);
-        case TILE_128x256: return launch_cfg<BITS, G, 128, 256, 1, 4, 32>(p, stream);
-        default:           return launch_cfg<BITS, G, 64, 256, 1, 4, 32>(p, stream);
+        case TILE_256x128: return launch_cfg<BITS, G, 256, 128, 2, 2, 32>(probs, count, stream);
+        case TILE_256x256: return launch_cfg<BITS, G, 256, 256, 2, 4, 64>(probs, count, stream);
+        case TILE_128x256: return launch_cfg<BITS, G, 128, 256, 1, 4, 32>(probs, count, stream);
+        default:           return launch_cfg<BITS, G, 64, 256, 1, 4, 32>(probs, count, stream);
     }
 }
 
@@ -356,19 +368,24 @@ int pick_tile_variant(int64_t M, int64_t N, int64_t K) {
     return TILE_64x256;
 }
 
-hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream) {
+hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
+                                   hipStream_t stream) {
     if (bits == 2) {
         switch (g) {
-            case 32: return launch_bits_g<2, 32>(p, variant, stream);
-            case 64: return launch_bits_g<2, 64>(p, variant, stream);
-            default: return launch_bits_g<2, 128>(p, variant, stream);
+            case 32: return launch_bits_g<2, 32>(probs, count, variant, stream);
+            case 64: return launch_bits_g<2, 64>(probs, count, variant, stream);
+            default: return launch_bits_g<2, 128>(probs, count, variant, stream);
         }
     }
     switch (g) {
-        case 32: return launch_bits_g<1, 32>(p, variant, stream);
-        case 64: return launch_bits_g<1, 64>(p, variant, stream);
-        default: return launch_bits_g<1, 128>(p, variant, stream);
+        case 32: return launch_bits_g<1, 32>(probs, count, variant, stream);
+        case 64: return launch_bits_g<1, 64>(probs, count, variant, stream);
+        default: return launch_bits_g<1, 128>(probs, count, variant, stream);
     }
+}
+
+hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream) {
+    return launch_gemm_tiled_group(&p, 1, g, bits, variant, stream);
 }
 
 }  // namespace lowbit

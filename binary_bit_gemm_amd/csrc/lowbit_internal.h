@@ -14,6 +14,16 @@ struct GemmProblem {
     int M, N, K;
 };
 
+// Several independent problems of one (g, bits) class in one launch.  Workgroup w of the
+// launch belongs to the first problem i with w < tile_end[i] (inclusive prefix sums of the
+// per-problem workgroup counts) and works on its local tile w - tile_end[i - 1].
+constexpr int kMaxGroup = 16;
+struct ProblemGroup {
+    GemmProblem p[kMaxGroup];
+    int tile_end[kMaxGroup];
+    int count;
+};
+
 hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
                        int32_t* bad_count, hipStream_t stream);
 hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
@@ -30,9 +40,13 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant,
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream);
 bool skinny_supported(int g, int bits);
 
-// Grouped launch: several problems of the same (g, bits) in one persistent launch.
+// Grouped launch: problems of one (g, bits) class; one launch per kernel family and per
+// kMaxGroup problems.
 hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int bits,
                                hipStream_t stream);
+hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
+                                   hipStream_t stream);
+hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
 
 int pick_tile_variant(int64_t M, int64_t N, int64_t K);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);

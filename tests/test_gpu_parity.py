@@ -279,3 +279,4 @@ def test_batched_matches_oracle_and_single_calls():
     for (x, w, s, y, g, bits), ref, single in zip(probs, refs, singles):
         yb = host_bits(y)
         _assert_parity(yb, ref, f"batched {tuple(x.shape)}x{w.shape[0]}")
+        assert np.array_equal(yb, single), f"batched differs from single call {tuple(x.shape)}"
