@@ -3,15 +3,17 @@
     python bench.py [--steps K] [--warmup W] [--workload res1024|res512|res512_binary|sweep|skinny]
 
 A step is one pass of the hot path over one batch of synthetic inputs that are already
-resident in HBM: every GEMM of the workload, each with its own weights.  Packing is the
-offline load-time step and runs before the timed region.
+resident in HBM: every GEMM of the workload, each with its own weights (the denoise-step
+workloads launch a double-stream block's image and text linear of one kind as one grouped
+call; --graph replays the step as one captured HIP graph).  Packing is the offline load-time step and
+runs before the timed region.
 
 Workloads (FLUX.2 Klein 4B MMDiT linears, hidden 3072):
   res1024        M = 4608 tokens (4096 image + 512 text) ternary g=64:
                  N x K = 3072x3072, 9216x3072, 18432x3072, 3072x9216, 3072x12288   (default)
   res512         M = 1536, the first four shapes, ternary g=64
   res512_binary  the same, binary g=64
-  sweep          the 80 quantised GEMMs of one denoise step at 1024x1024
+  sweep          the 80 quantised GEMMs of one denoise step at 1024x1024 (60 launches)
   skinny         the same 80 GEMMs at M = 16 (HBM-bound; reports GB/s)
 
 Prints one JSON line.  Inputs are seeded and synthetic: X ~ N(0,1) -> bf16, codes i.i.d.
@@ -60,14 +62,17 @@ METRIC = "lowbit GEMM TFLOP/s and % of bf16 MFMA peak (M=4608, ternary g=64)"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
                     choices=["res1024", "res512", "res512_binary", "sweep", "skinny"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of X in the CPU oracle sample (0 = all rows of the workload)")
+    ap.add_argument("--graph", action="store_true",
+                    help="launch each step as one captured HIP graph (measured slightly slower than eager launches "
+                         "on these workloads, so off by default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -161,70 +166,107 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2}))
         return
 
+    import workloads as W
     probs = problems_for(a.workload)
+    groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
     bufs = make_device_inputs(probs, a.seed)
-    stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for i, (x, w, s, y, g, bits) in enumerate(bufs):
-            if events is not None:
-                events[i][0].record(stream)
+    def launch(grp):
+        if len(grp) == 1:
+            x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm(x, w, s, g, bits, out=y)
-            if events is not None:
-                events[i][1].record(stream)
+        else:
+            lb.gemm_batched([bufs[i] for i in grp])
+
+    def step():
+        for grp in groups:
+            launch(grp)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, wall clock between two synchronisations
+    # optionally the step as one HIP graph (captured on a side stream, replayed on the current one)
+    graph = None
+    if a.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    run_step = graph.replay if graph is not None else step
+
+    # timed region: exactly `steps` steps between two synchronisations, bracketed by HIP
+    # events on the stream the launches go to
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for _ in range(a.steps):
-        step()
+        run_step()
+    e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    event_ms = e0.elapsed_time(e1) / a.steps
 
-    # per-launch kernel durations with HIP events on the launch stream (separate pass)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in bufs]
+    # per-call kernel durations with HIP events around each eager call (separate pass; the
+    # breakdown only -- host launch time can show up in it for calls of a few microseconds)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
           for _ in range(a.steps)]
     for k in range(a.steps):
-        step(ev[k])
+        for i, grp in enumerate(groups):
+            ev[k][i][0].record(stream)
+            launch(grp)
+            ev[k][i][1].record(stream)
     torch.cuda.synchronize()
-    launch_ms = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(a.steps)) / a.steps
-                 for i in range(len(bufs))]
+    call_ms = [sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(a.steps)) / a.steps
+               for i in range(len(groups))]
 
     flops_step = sum(p.flops for p in probs)
     bytes_step = sum(p.bytes_moved() for p in probs)
     ms_per_step = elapsed * 1e3 / a.steps
     tflops = flops_step / (elapsed / a.steps) / 1e12
-    kern_ms = sum(launch_ms)
-    kern_tflops = flops_step / (kern_ms * 1e-3) / 1e12
-    kern_gbs = bytes_step / (kern_ms * 1e-3) / 1e9
+    launches = len(groups)
+    # dominant kernel: every launch of the step is the same kernel family; its average launch
+    # duration is the event-timed step divided by the launches per step
+    launch_ms = event_ms / launches
+    kern_tflops = flops_step / (event_ms * 1e-3) / 1e12
+    kern_gbs = bytes_step / (event_ms * 1e-3) / 1e9
+    traffic = measured_traffic(a.workload)
 
     if a.workload == "skinny":
         metric, value, unit = "lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)", \
             bytes_step / (elapsed / a.steps) / 1e9, "GB/s"
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(a.workload),
-                "algorithmic_bytes_per_launch": bytes_step // len(probs)}
+                "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         metric = METRIC if a.workload == "res1024" else METRIC.replace("(M=4608, ternary g=64)", f"({a.workload})")
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.workload),
-                "algorithmic_bytes_per_launch": bytes_step // len(probs)}
-    variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
+                "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    roof.update({"kernel": sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs}),
+                 "launches_per_step": launches, "avg_launch_us": round(1e3 * launch_ms, 2),
+                 "algorithmic_flop_per_launch": flops_step // launches,
+                 "algorithmic_bytes_per_launch": bytes_step // launches})
     out = {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": a.workload, "gemms_per_step": len(probs),
+        "config": {"workload": a.workload, "gemms_per_step": len(probs), "launches_per_step": launches,
+                   "graph": graph is not None,
                    "shapes": sorted({f"{p.M}x{p.N}x{p.K}" for p in probs}),
                    "bits": sorted({p.bits for p in probs}), "g": sorted({p.g for p in probs}),
                    "flop_per_step": flops_step, "bytes_per_step": bytes_step,
                    "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                   "kernel_variants": variants,
-                   "per_gemm_us": [round(1e3 * t, 2) for t in launch_ms[:8]]},
+                   "pct_hbm_peak": round(100 * bytes_step / (elapsed / a.steps) / 1e9 / PEAK_HBM_GBS, 2),
+                   "per_call_us": [round(1e3 * t, 2) for t in call_ms[:8]]},
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

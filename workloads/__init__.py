@@ -154,6 +154,25 @@ def denoise_step_sweep(M_img: int = 4096, M_txt: int = 512, bits: int = TERNARY,
     return probs
 
 
+def step_groups(probs: List[Problem]) -> List[List[int]]:
+    """Indices of `probs` (a denoise_step_sweep list) in launch order, grouped the way the
+    model allows: a double-stream block's image and text linear of one kind are independent
+    and go together; everything else is sequential and goes alone."""
+    groups: List[List[int]] = []
+    pending: dict = {}
+    for i, p in enumerate(probs):
+        parts = p.name.split("_", 2)
+        if p.name.startswith("d") and len(parts) == 3:
+            key = (parts[0], parts[2])
+            if key in pending:
+                groups[pending.pop(key)].append(i)
+                continue
+            pending[key] = len(groups)
+        groups.append([i])
+    # within a block: qkv, proj, mlp_in, mlp_out pairs in that order
+    return groups
+
+
 CONFIGS = {
     "tiny": TINY,
     "res512_ternary": RES512_TERNARY,
