@@ -31,7 +31,7 @@ class LowbitError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.environ.get("LOWBIT_LIBRARY", os.path.join(_HERE, "liblowbit.so"))
+    return os.environ.get("LOWBIT_LIBRARY") or os.path.join(_HERE, "liblowbit.so")
 
 
 def lib() -> ctypes.CDLL:

@@ -1,0 +1,333 @@
+// Packed ternary GEMM on 16x16x32 MFMA blocks: Y[M,N] = X[M,K] . dequant(W)[N,K]^T, for scale
+// groups of 64 or 128.
+//
+// Why a second tile kernel: with 32x32 blocks a workgroup tile is a multiple of 32 in both
+// directions and 8 waves want a multiple of 8 blocks, so 4608 x 3072 outputs come out as 216
+// tiles of 256 x 256 on 256 compute units -- 16% of the chip idles.  16x16 blocks allow a
+// 288 x 192 tile (12 waves of 96 x 48): 4608 x 3072 is then exactly 256 tiles, 4608 x 9216
+// and 4608 x 18432 whole multiples of 256.  Per FLOP the 16x16x32 instruction needs the same
+// operand bytes, the same code expansion and the same scale FMAs as the 32x32x16 one.
+//
+// Data movement is that of the 32x32 kernel (direct-to-LDS copies of X per 64-element step,
+// of packed weights in 64-byte row blocks = 4 steps, of scales in 8-group blocks; everything
+// double-buffered and XOR-swizzled in 16-byte chunks).  K order inside a step: lane quarter q
+// of a 16x16x32 block takes word q of each weight row's 16-byte step chunk (codes 16q..16q+15
+// of the step) and, in the two MFMAs of the step, its first and second eight codes; the
+// activation operand of quarter q is therefore chunk 2q + j of the row's 128-byte step.  A
+// step is one scale group of 64 (or half of a group of 128, whose scale then multiplies each
+// half: w = scale_g * b, model card "Binary Weight Representation: 1-bit g128").
+#include "lowbit_device.h"
+#include "lowbit_internal.h"
+
+namespace lowbit {
+namespace {
+
+constexpr int KS = 64;                 // K elements per step
+constexpr int kRowBytes = KS * 2;      // one bf16 row of an X tile per step
+constexpr int kXChunks = kRowBytes / 16;
+constexpr int kWB = 64;                // packed bytes per weight row and block (4 ternary steps)
+constexpr int kWSpb = kWB / 16;        // steps per weight block
+constexpr int kSGpb = 8;               // scale groups per scale block
+
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
+
+// Chunk c of weight row r within a block sits at position c ^ ((r >> 2) & 3): the 16 rows x 4
+// words one ds_read_b32 touches land in 64 different banks.
+__device__ __forceinline__ int w_pos(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+struct Cfg16 {
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int MB = WM / 16, NB = WN / 16;
+    static constexpr int X_TILE = BM * kRowBytes;
+    static constexpr int X_SLOTS = BM * kXChunks;            // 16-byte copies per step
+    static constexpr int W_BLOCK = BN * kWB;
+    static constexpr int W_SLOTS = BN * (kWB / 16);
+    static constexpr int S_BLOCK = BN * 32;                  // two aligned 16-byte windows per row
+    static constexpr int S_SLOTS = BN * 2;
+    static_assert(WM % 16 == 0 && WN % 16 == 0 && MB >= 1 && NB >= 1, "wave tile");
+    static_assert(THREADS % kXChunks == 0, "a thread copies one chunk column of X");
+    static_assert(G == 64 || G == 128, "scale groups of 64 or 128");
+};
+
+template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(ProblemGroup grp) {
+    using C = Cfg16<G, BM, BN, WAVES_M, WAVES_N>;
+    __shared__ __attribute__((aligned(16))) unsigned char xa0[C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char xa1[C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char wk0[C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char wk1[C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk0[C::S_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk1[C::S_BLOCK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
+    const int q = lane >> 4, l16 = lane & 15;
+
+    const int t = xcd_remap(blockIdx.x, grp.tile_end[grp.count - 1]);
+    int pi = 0;
+    while (pi + 1 < grp.count && t >= grp.tile_end[pi]) ++pi;
+    const GemmProblem p = grp.p[pi];
+    const int tile = t - (pi > 0 ? grp.tile_end[pi - 1] : 0);
+    const int M = p.M, N = p.N, K = p.K;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tm = tile / tiles_n, tn = tile % tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
+
+    const int kgroups = K / G;
+    const int ksteps = K / KS;
+    const uint32_t w_row_bytes = uint32_t(K) / 4u;
+    const uint32_t s_row_bytes = uint32_t(kgroups) * 2u;
+
+    // ---- X: thread copies chunk position tid % 8 of rows tid / 8 + i * (THREADS / 8) ----
+    constexpr int kRowsPerRound = C::THREADS / kXChunks;
+    const int r_first = tid / kXChunks;
+    const uint32_t x_voff = uint32_t(r_first) * uint32_t(K) * 2u +
+                            uint32_t((tid % kXChunks) ^ lds_swizzle(r_first)) * 16u;
+    const uint32_t x_row_step = uint32_t(kRowsPerRound) * uint32_t(K) * 2u;
+    const unsigned char* x_tile = reinterpret_cast<const unsigned char*>(p.X) + size_t(m0) * size_t(K) * 2;
+    const uint32_t x_tile_bytes = uint32_t(M - m0 < BM ? M - m0 : BM) * uint32_t(K) * 2u;
+    auto issue_x = [&](int step, unsigned char* buf) {
+        const uint32_t kb = uint32_t(step) * KS * 2u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(x_tile + kb, x_tile_bytes - kb);
+#pragma unroll
+        for (int i = 0; i < (C::X_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
+            if (i * C::THREADS + wave_u * 64 < C::X_SLOTS)
+                dma16(rs, buf + (i * C::THREADS + wave_u * 64) * 16, x_voff + uint32_t(i) * x_row_step, 0);
+        }
+    };
+
+    // ---- packed weights: block b = steps [4b, 4b+4) of the tile's BN rows, 64 bytes per row.
+    // Copy slot s = row s / 4, stored position s % 4 (holding source chunk w_pos(row, s % 4)).
+    // Rows past N re-read row N-1.
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(N) * w_row_bytes);
+    auto issue_w = [&](int block, unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < (C::W_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
+            const int slot0 = i * C::THREADS + wave_u * 64;
+            if (slot0 < C::W_SLOTS) {
+                const int slot = slot0 + lane;
+                const int r = slot >> 2;
+                int n = n0 + r;
+                n = n < N ? n : N - 1;
+                const uint32_t voff = uint32_t(n) * w_row_bytes + uint32_t(w_pos(r, slot & 3) * 16);
+                dma16(w_rs, buf + slot0 * 16, voff, __builtin_amdgcn_readfirstlane(block * kWB));
+            }
+        }
+    };
+
+    // ---- scales: block b = groups [8b, 8b+8) of the tile's BN rows, as two aligned 16-byte
+    // windows per row; the row's group 8b sits (row offset & 15) bytes in.
+    const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(p.S, uint32_t(N) * s_row_bytes);
+    auto issue_s = [&](int block, unsigned char* buf) {
+#pragma unroll
+        for (int i = 0; i < (C::S_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
+            const int slot0 = i * C::THREADS + wave_u * 64;
+            if (slot0 < C::S_SLOTS) {
+                const int slot = slot0 + lane;
+                const int r = slot >> 1;
+                int n = n0 + r;
+                n = n < N ? n : N - 1;
+                const uint32_t start = uint32_t(n) * s_row_bytes + uint32_t(block) * 16u;
+                const uint32_t voff = (start & ~15u) + uint32_t(slot & 1) * 16u;
+                dma16(s_rs, buf + slot0 * 16, voff, 0);
+            }
+        }
+    };
+
+    // Per-lane LDS offsets: weight row of each column block, its scale window.
+    int w_rd[C::NB], s_rd[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+        const int r = wn0 + nb * 16 + l16;
+        int n = n0 + r;
+        n = n < N ? n : N - 1;
+        w_rd[nb] = r * kWB + 4 * q;
+        s_rd[nb] = r * 32 + int((uint32_t(n) * s_row_bytes) & 15u);
+    }
+
+    static_assert(C::WM % 16 == 0, "row blocks start at multiples of 16");
+    int x_rd[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) x_rd[j] = x_off(wm0 + l16, 2 * q + j);
+
+    f32x4_t acc[C::MB][C::NB];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // A step's words and scales are read from LDS before any copy of the step is issued (the
+    // compiler cannot tell which of the two buffers a step reads).
+    struct Ops {
+        uint32_t w[C::NB];
+        float sc[C::NB];
+    };
+    auto read_operands = [&](const unsigned char* wt, const unsigned char* st, int step, Ops& o) {
+        const int wj = step % kWSpb;
+        const int grp_in_block = (step * KS / G) & (kSGpb - 1);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            const int r = wn0 + nb * 16 + l16;
+            o.w[nb] = *reinterpret_cast<const uint32_t*>(wt + w_rd[nb] + (w_pos(r, wj) << 4));
+            // x 1/2: the operand holds 2c.  Also keeps the conversion out of the FMA (an fp16
+            // operand makes it v_fma_mix_f32, whose result does not share the accumulator's
+            // register and doubles the accumulator registers across the unrolled steps).
+            o.sc[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + grp_in_block * 2)) * 0.5f;
+        }
+    };
+
+    auto compute = [&](const unsigned char* xt, const Ops& o) {
+        u32x4_t bfr[C::NB][2];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            uint32_t d[8];
+            expand_ternary_word(o.w[nb], d);
+            bfr[nb][0] = u32x4_t{d[0], d[1], d[2], d[3]};
+            bfr[nb][1] = u32x4_t{d[4], d[5], d[6], d[7]};
+        }
+        // Row blocks in order; within one, the MFMA pair of block (mb, nb) is issued before the
+        // scale FMAs of the previous block, which use the other partial-sum registers.  The
+        // activation operands of row block mb + 1 are read while row block mb computes.  Row
+        // blocks start at multiples of 16, so the swizzle of row wm0 + 16 mb + l16 does not
+        // depend on mb: one base address per chunk, the row block as an immediate offset.
+        f32x4_t tmp[2];
+        bf16x8_t afr[2][2];  // [row block parity][k half]
+#pragma unroll
+        for (int j = 0; j < 2; ++j) afr[0][j] = *reinterpret_cast<const bf16x8_t*>(xt + x_rd[j]);
+        int pb = -1;  // previous block, its partial sum in tmp[pb & 1]
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+            if (mb + 1 < C::MB) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    afr[(mb + 1) & 1][j] = *reinterpret_cast<const bf16x8_t*>(xt + x_rd[j] + (mb + 1) * 16 * kRowBytes);
+            }
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int b = mb * C::NB + nb;
+                f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mb & 1][j], __builtin_bit_cast(bf16x8_t, bfr[nb][j]), v, 0,
+                                                                0, 0);
+                tmp[b & 1] = v;
+                if (pb >= 0) {
+                    const int pm = pb / C::NB, pn = pb % C::NB;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[pm][pn][i] = __builtin_fmaf(o.sc[pn], tmp[pb & 1][i], acc[pm][pn][i]);
+                }
+                pb = b;
+            }
+        }
+        {
+            const int pm = pb / C::NB, pn = pb % C::NB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[pm][pn][i] = __builtin_fmaf(o.sc[pn], tmp[pb & 1][i], acc[pm][pn][i]);
+        }
+        // An empty side-effecting use of every accumulator closes the step: otherwise the
+        // compiler sinks this step's scale FMAs past the barrier into the next step's first
+        // block, and all partial sums of the step stay live at once.
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) asm volatile("" ::"v"(acc[mb][nb]));
+    };
+
+    auto w_buf = [&](int step) -> unsigned char* { return ((step / kWSpb) & 1) ? wk1 : wk0; };
+    auto s_block = [&](int step) { return (step * KS / G) / kSGpb; };
+    auto s_buf = [&](int step) -> unsigned char* { return (s_block(step) & 1) ? sk1 : sk0; };
+    const int w_blocks = (ksteps + kWSpb - 1) / kWSpb;
+    const int s_blocks = (kgroups + kSGpb - 1) / kSGpb;
+
+    auto prefetch_x = [&](int step, unsigned char* xbuf) {
+        if (step + 1 < ksteps) issue_x(step + 1, xbuf);
+    };
+    auto prefetch_blocks = [&](int step) {
+        if (step % kWSpb == 0 && step / kWSpb + 1 < w_blocks) issue_w(step / kWSpb + 1, w_buf(step + kWSpb));
+        const int sb = s_block(step);
+        if ((step == 0 || s_block(step - 1) != sb) && sb + 1 < s_blocks) issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+    };
+
+    issue_x(0, xa0);
+    issue_w(0, wk0);
+    issue_s(0, sk0);
+    wait_vmcnt0();
+    __syncthreads();
+
+    // Steps in pairs (static LDS buffers, so the compiler's wait insertion stays exact) with a
+    // single loop exit; an odd last step runs after the loop.  A break between the two steps
+    // of an iteration made the register allocator give every accumulator a second register
+    // and copy it back each iteration.
+    Ops ops;
+    int step = 0;
+#pragma nounroll
+    for (; step + 1 < ksteps; step += 2) {
+        read_operands(w_buf(step), s_buf(step), step, ops);
+        prefetch_x(step, xa1);
+        prefetch_blocks(step);
+        compute(xa0, ops);
+        wait_vmcnt0();
+        __syncthreads();
+        read_operands(w_buf(step + 1), s_buf(step + 1), step + 1, ops);
+        prefetch_x(step + 1, xa0);
+        prefetch_blocks(step + 1);
+        compute(xa1, ops);
+        wait_vmcnt0();
+        __syncthreads();
+    }
+    if (step < ksteps) {
+        read_operands(w_buf(step), s_buf(step), step, ops);
+        compute(xa0, ops);
+    }
+
+    // ---- epilogue: 16x16 block layout: lane holds column lane % 16, rows 4 * (lane / 16) + i ----
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            const int n = n0 + wn0 + nb * 16 + l16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm0 + mb * 16 + 4 * q + i;
+                if (m < M) p.Y[int64_t(m) * N + n] = float_to_bf16_bits(acc[mb][nb][i]);
+            }
+        }
+    }
+}
+
+template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
+    ProblemGroup grp{};
+    int total = 0;
+    for (int i = 0; i < count; ++i) {
+        grp.p[i] = probs[i];
+        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + BN - 1) / BN);
+        grp.tile_end[i] = total;
+    }
+    grp.count = count;
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BM, BN, WAVES_M, WAVES_N>), dim3(total), dim3(64 * WAVES_M * WAVES_N),
+                       0, stream, grp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool tile16_supported(int g, int bits) { return bits == 2 && (g == 64 || g == 128); }
+
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, hipStream_t stream) {
+    // 288 x 192 in 12 waves of 96 x 48: LDS 72 KB (X) + 24 KB (W) + 12 KB (S)
+    return g == 64 ? launch_cfg16<64, 288, 192, 3, 4>(probs, count, stream)
+                   : launch_cfg16<128, 288, 192, 3, 4>(probs, count, stream);
+}
+
+}  // namespace lowbit

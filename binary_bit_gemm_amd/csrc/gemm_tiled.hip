@@ -361,15 +361,64 @@ hipError_t launch_bits_g(const GemmProblem* probs, int count, int variant, hipSt
 
 }  // namespace
 
-int pick_tile_variant(int64_t M, int64_t N, int64_t K) {
-    (void)N; (void)K;
-    if (M >= 1024) return TILE_256x256;
-    if (M >= 256) return TILE_128x256;
-    return TILE_64x256;
+namespace {
+
+struct TileShape {
+    int variant, bm, bn, per_cu;  // workgroups resident per compute unit
+    float eff;                    // relative per-FLOP efficiency of the tile (measured order)
+};
+
+constexpr TileShape kTiles[] = {
+    {TILE_256x256, 256, 256, 1, 1.00f},
+    {TILE_288x192, 288, 192, 1, 1.00f},
+    {TILE_128x256, 128, 256, 2, 0.92f},
+    {TILE_64x256, 64, 256, 2, 0.75f},
+};
+
+constexpr int kComputeUnits = 256;
+
+}  // namespace
+
+int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
+    int best = TILE_64x256;
+    double best_cost = 0.0;
+    for (const TileShape& t : kTiles) {
+        if (t.variant == TILE_288x192 && !tile16_supported(g, bits)) continue;
+        int64_t tiles = 0;
+        for (int i = 0; i < count; ++i)
+            tiles += int64_t((probs[i].M + t.bm - 1) / t.bm) * ((probs[i].N + t.bn - 1) / t.bn);
+        const int64_t slots = int64_t(kComputeUnits) * t.per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double cost = double(rounds) * t.per_cu * t.bm * t.bn / t.eff;
+        if (best_cost == 0.0 || cost < best_cost) {
+            best = t.variant;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
+    const GemmProblem p{nullptr, nullptr, nullptr, nullptr, int(M), int(N), int(K)};
+    return pick_tile_variant(&p, 1, g, bits);
+}
+
+const char* tile_variant_name(int variant) {
+    switch (variant) {
+        case TILE_256x128: return "tile256x128";
+        case TILE_256x256: return "tile256x256";
+        case TILE_128x256: return "tile128x256";
+        case TILE_288x192: return "tile288x192";
+        default: return "tile64x256";
+    }
 }
 
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream) {
+    if (variant == TILE_288x192) {
+        if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, stream);
+        variant = TILE_256x256;
+    }
     if (bits == 2) {
         switch (g) {
             case 32: return launch_bits_g<2, 32>(probs, count, variant, stream);

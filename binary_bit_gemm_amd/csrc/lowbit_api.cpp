@@ -47,7 +47,8 @@ int device_check() {
     return r == 1 ? LOWBIT_OK : LOWBIT_E_UNSUPPORTED;
 }
 
-// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | tile256 | tile256w | tile128 | tile64
+// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | tile256 | tile256w | tile128 | tile64 |
+// tile288 (the last falls back to tile256w where the 16x16 kernel does not apply)
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
@@ -56,6 +57,7 @@ int forced_variant() {
     if (std::strcmp(v, "tile256w") == 0) return lowbit::TILE_256x256;
     if (std::strcmp(v, "tile128") == 0) return lowbit::TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return lowbit::TILE_64x256;
+    if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
     return -1;
 }
 
@@ -64,7 +66,7 @@ int choose_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     if (f == 100 && lowbit::use_skinny(M, N, K, g, bits)) return 100;
     if (f >= 0 && f != 100) return f;
     if (lowbit::use_skinny(M, N, K, g, bits)) return 100;
-    return lowbit::pick_tile_variant(M, N, K);
+    return lowbit::pick_tile_variant(M, N, K, g, bits);
 }
 
 __global__ void zero_fill_kernel(uint16_t* y, int64_t n) {
@@ -139,13 +141,10 @@ int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, cons
 }
 
 const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
-    switch (choose_variant(M, N, K, g, bits)) {
-        case 100: return "skinny";
-        case lowbit::TILE_256x128: return "tile256x128";
-        case lowbit::TILE_256x256: return "tile256x256";
-        case lowbit::TILE_128x256: return "tile128x256";
-        default: return "tile64x256";
-    }
+    int v = choose_variant(M, N, K, g, bits);
+    if (v == 100) return "skinny";
+    if (v == lowbit::TILE_288x192 && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
+    return lowbit::tile_variant_name(v);
 }
 
 int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,

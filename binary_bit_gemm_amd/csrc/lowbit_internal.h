@@ -29,8 +29,9 @@ hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, i
 hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
                          hipStream_t stream);
 
-// Tiled MFMA kernel (LDS-staged X, packed weights and scales).  `variant` selects the tile.
-enum TileVariant { TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3 };
+// Tiled MFMA kernels (LDS-staged X, packed weights and scales).  `variant` selects the tile;
+// TILE_288x192 is the 16x16x32-block kernel (ternary, g = 64 or 128 only).
+enum TileVariant { TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4 };
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
@@ -48,7 +49,12 @@ hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, i
                                    hipStream_t stream);
 hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
 
-int pick_tile_variant(int64_t M, int64_t N, int64_t K);
+// Tile for a group of problems: fewest estimated rounds x tile work over the whole group.
+int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits);
+int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
+const char* tile_variant_name(int variant);
+bool tile16_supported(int g, int bits);
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit

@@ -88,10 +88,15 @@ def test_gemm_rejects_before_touching_the_device():
 
 
 def test_variant_choice():
-    assert lb.variant(4608, 18432, 3072) == "tile256x256"
-    assert lb.variant(1536, 3072, 3072) == "tile256x256"
-    assert lb.variant(512, 3072, 3072) == "tile128x256"
-    assert lb.variant(64, 256, 256) == "tile64x256"
+    """Tile choice: fewest rounds of tiles over 256 compute units, weighted by tile work.
+    4608 x 3072 is 216 tiles of 256 x 256 (40 units idle) but exactly 256 of 288 x 192."""
+    assert lb.variant(4608, 3072, 3072, 64, 2) == "tile288x192"
+    assert lb.variant(4608, 18432, 3072, 64, 2) == "tile288x192"
+    assert lb.variant(4608, 3072, 12288, 128, 2) == "tile288x192"
+    # the 16x16-block kernel is ternary g = 64 / 128 only
+    assert lb.variant(4608, 3072, 3072, 64, 1) == "tile256x256"
+    assert lb.variant(4608, 3072, 3072, 32, 2) == "tile256x256"
+    assert lb.variant(64, 256, 256, 64, 2).startswith("tile")
 
 
 def test_skinny_variant_choice():

@@ -102,7 +102,7 @@ def test_gemm_small(M, N, K, g, bits):
     _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{M}x{N}x{K} g{g} b{bits}")
 
 
-@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "skinny"])
+@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "tile288", "skinny"])
 @pytest.mark.parametrize("M", [16, 300, 600])
 def test_every_variant(variant, M, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
