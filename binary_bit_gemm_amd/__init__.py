@@ -89,8 +89,18 @@ def unpack(words, K: int, bits: int):
     return codes
 
 
-def gemm(x, words, scales, g: int, bits: int, out=None):
-    """Y[M, N] = X[M, K] . dequant(W)[N, K]^T in bf16 (see include/lowbit.h)."""
+def workspace_size(M: int, N: int, K: int, g: int = 64, bits: int = 2) -> int:
+    """Bytes of workspace lowbit_gemm_ex can use for this shape (0: none needed)."""
+    return int(lib().lowbit_workspace_size(M, N, K, g, bits))
+
+
+def gemm(x, words, scales, g: int, bits: int, out=None, workspace=None):
+    """Y[M, N] = X[M, K] . dequant(W)[N, K]^T in bf16 (see include/lowbit.h).
+
+    `workspace`: an optional zero-filled device tensor (any dtype) of at least
+    workspace_size(M, N, K, g, bits) bytes; it lets skinny problems split K across
+    workgroups (lowbit_gemm_ex).  Reuse it between calls; do not share it between calls
+    that run concurrently."""
     torch = _torch()
     _require(x, torch.bfloat16, "x")
     _require(words, torch.int32, "words")
@@ -107,10 +117,20 @@ def gemm(x, words, scales, g: int, bits: int, out=None):
         _require(out, torch.bfloat16, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [M, N]")
-    st = lib().lowbit_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
-                           ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-                           M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
-    _check(st, "lowbit_gemm")
+    if workspace is None:
+        st = lib().lowbit_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                               ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                               M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
+        _check(st, "lowbit_gemm")
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        st = lib().lowbit_gemm_ex(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  M, N, K, g, bits, ctypes.c_void_p(workspace.data_ptr()), nbytes,
+                                  ctypes.c_void_p(_stream_ptr(x.device)))
+        _check(st, "lowbit_gemm_ex")
     return out
 
 

@@ -58,13 +58,30 @@ int forced_variant() {
     if (std::strcmp(v, "tile128") == 0) return lowbit::TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return lowbit::TILE_64x256;
     if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
+    if (std::strcmp(v, "ring") == 0) return 101;
     return -1;
+}
+
+// Largest K split of the ring kernel (LOWBIT_RING_MAX_SPLITS, for A/B runs and tests).
+int ring_max_splits() {
+    const char* v = std::getenv("LOWBIT_RING_MAX_SPLITS");
+    const int n = v != nullptr ? std::atoi(v) : 0;
+    return n >= 1 && n <= 64 ? n : 16;
+}
+
+// Ring kernel without a workspace: only when it fills the machine without splitting K.
+bool ring_without_workspace(int64_t M, int64_t N, int64_t K, int g, int bits) {
+    if (!lowbit::ring_supported(M, N, K, g, bits)) return false;
+    const lowbit::RingPlan plan = lowbit::plan_ring(N, K, 1);
+    return plan.tiles * plan.splits >= 384;
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     const int f = forced_variant();
+    if (f == 101 && lowbit::ring_supported(M, N, K, g, bits)) return 101;
     if (f == 100 && lowbit::use_skinny(M, N, K, g, bits)) return 100;
-    if (f >= 0 && f != 100) return f;
+    if (f >= 0 && f != 100 && f != 101) return f;
+    if (ring_without_workspace(M, N, K, g, bits)) return 101;
     if (lowbit::use_skinny(M, N, K, g, bits)) return 100;
     return lowbit::pick_tile_variant(M, N, K, g, bits);
 }
@@ -83,8 +100,12 @@ int launch_one(const lowbit::GemmProblem& p, int g, int bits, hipStream_t stream
         e = hipGetLastError();
     } else {
         const int v = choose_variant(p.M, p.N, p.K, g, bits);
-        e = v == 100 ? lowbit::launch_gemm_skinny(p, g, bits, stream)
-                     : lowbit::launch_gemm_tiled(p, g, bits, v, stream);
+        if (v == 101) {
+            e = lowbit::launch_gemm_ring(p, g, lowbit::plan_ring(p.N, p.K, 1), nullptr, stream);
+        } else {
+            e = v == 100 ? lowbit::launch_gemm_skinny(p, g, bits, stream)
+                         : lowbit::launch_gemm_tiled(p, g, bits, v, stream);
+        }
     }
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
@@ -143,6 +164,7 @@ int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, cons
 const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     int v = choose_variant(M, N, K, g, bits);
     if (v == 100) return "skinny";
+    if (v == 101) return "ring";
     if (v == lowbit::TILE_288x192 && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
     return lowbit::tile_variant_name(v);
 }
@@ -175,6 +197,30 @@ int lowbit_gemm(const void* X, const uint32_t* W, const void* S, void* Y,
     lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
                           static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
     return launch_one(p, g, bits, static_cast<hipStream_t>(stream));
+}
+
+size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits) {
+    if (lowbit_check_gemm_args(nullptr, nullptr, nullptr, nullptr, 0, N, K, g, bits) != LOWBIT_OK) return 0;
+    if (!lowbit::ring_supported(M, N, K, g, bits)) return 0;
+    return lowbit::ring_workspace_bytes(lowbit::plan_ring(N, K, ring_max_splits()), N);
+}
+
+int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y, int64_t M, int64_t N, int64_t K,
+                   int g, int bits, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
+    if (K == 0 || !lowbit::ring_supported(M, N, K, g, bits) || forced_variant() >= 0)
+        return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
+    const lowbit::RingPlan plan = lowbit::plan_ring(N, K, ring_max_splits());
+    if (plan.splits > 1 && (workspace == nullptr || workspace_bytes < lowbit::ring_workspace_bytes(plan, N)))
+        return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                          static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
+    const hipError_t e = lowbit::launch_gemm_ring(p, g, plan, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 
 int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream) {

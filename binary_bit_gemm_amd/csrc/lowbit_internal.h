@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lowbit {
@@ -40,6 +41,24 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant,
 // tile.
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream);
 bool skinny_supported(int g, int bits);
+
+// Ring kernel (ternary, M <= 16, g = 64 / 128, K % 256 == 0, N % 64 == 0): deep LDS load
+// ring, optional split-K across workgroups through a caller-provided workspace.
+struct RingArgs {
+    GemmProblem p;
+    int splits;           // workgroups per column tile along K
+    float* ws;            // fp32 partial sums (splits > 1)
+    uint32_t* counters;   // one arrival counter per column tile, zero between calls
+};
+struct RingPlan {
+    int nw;      // 16-column blocks per wave (a column tile is 4 * nw blocks)
+    int splits;  // workgroups per column tile along K
+    int tiles;   // column tiles
+};
+bool ring_supported(int64_t M, int64_t N, int64_t K, int g, int bits);
+RingPlan plan_ring(int64_t N, int64_t K, int max_splits);
+size_t ring_workspace_bytes(const RingPlan& plan, int64_t N);
+hipError_t launch_gemm_ring(const GemmProblem& p, int g, const RingPlan& plan, void* workspace, hipStream_t stream);
 
 // Grouped launch: problems of one (g, bits) class; one launch per kernel family and per
 // kMaxGroup problems.

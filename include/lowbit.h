@@ -37,7 +37,8 @@
  *     return means nothing was launched.
  *   - Supported: bits in {1, 2}; g in {32, 64, 128}; K % g == 0; N % 16 == 0; M >= 0
  *     (M == 0 or N == 0 is a no-op); M, N, K < 2^31; the current device is gfx950.
- *   - The library allocates no device memory and uses no hidden workspace.
+ *   - The library allocates no device memory and uses no hidden workspace; the only
+ *     workspace is the one a caller passes to lowbit_gemm_ex.
  *   - Results are deterministic: the same inputs give bitwise the same Y on every run.
  */
 #ifndef LOWBIT_H
@@ -112,6 +113,29 @@ typedef struct lowbit_problem {
  * Every problem is validated as in lowbit_gemm before anything is launched.
  */
 int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream);
+
+/*
+ * lowbit_workspace_size -- bytes of caller-provided device workspace with which
+ * lowbit_gemm_ex can split K across workgroups for this shape (0: it never needs one).
+ * The split applies to skinny ternary problems (M <= 16, g = 64 or 128, K % 256 == 0,
+ * N % 64 == 0); there the fp32 partial sums of the K slices are added in a fixed order, so
+ * the result is deterministic (it can differ in the last bits from lowbit_gemm's, which
+ * splits K differently).  Returns 0 for invalid arguments.
+ */
+size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits);
+
+/*
+ * lowbit_gemm_ex -- lowbit_gemm with a caller-provided workspace.
+ *   workspace        device memory of at least lowbit_workspace_size(...) bytes, 16-byte
+ *                    aligned, ZERO-FILLED before its first use.  Every call leaves the
+ *                    workspace's counters at zero again, so it can be reused as is.  Calls
+ *                    that share a workspace must not run concurrently.
+ *   workspace_bytes  its size.  With a NULL or too small workspace (or for shapes that need
+ *                    none) the call is exactly lowbit_gemm.
+ */
+int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y,
+                   int64_t M, int64_t N, int64_t K, int g, int bits,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */

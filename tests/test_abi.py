@@ -103,7 +103,7 @@ def test_skinny_variant_choice():
     """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) when a 16-byte chunk of
     a packed row lies in one scale group and K is a whole number of 64-byte row steps."""
     assert lb.variant(16, 3072, 3072, 64, 2) == "skinny"
-    assert lb.variant(1, 27648, 3072, 128, 2) == "skinny"
+    assert lb.variant(1, 3072, 3072, 128, 2) == "skinny"
     assert lb.variant(32, 3072, 12288, 64, 2) == "skinny"
     assert lb.variant(33, 3072, 3072, 64, 2) == "tile64x256"
     assert lb.variant(16, 3072, 3072, 32, 2) == "tile64x256"     # group of 32 < chunk of 64
@@ -112,3 +112,30 @@ def test_skinny_variant_choice():
     assert lb.variant(16, 3072, 3072, 64, 1) == "tile64x256"     # binary chunk is 128 codes
     assert lb.variant(16, 3072, 2816, 128, 1) == "tile64x256"    # K % 512 != 0
     assert lb.variant(17, 3072, 3072, 128, 1) == "tile64x256"
+
+
+def test_ring_variant_and_workspace_size():
+    """The ring kernel takes M <= 16 ternary g = 64 / 128 problems; without a workspace only
+    when it fills the machine unsplit (N = 27648: 432 workgroups).  Its split-K workspace is
+    sized on the host: arrival counters + fp32 partials of 16 rows per split."""
+    assert lb.variant(16, 27648, 3072, 64, 2) == "ring"
+    assert lb.variant(16, 27648, 3072, 128, 2) == "ring"
+    assert lb.variant(17, 27648, 3072, 64, 2) == "skinny"
+    assert lb.variant(16, 27648, 3072, 128, 1) == "skinny"
+    n = lb.workspace_size(16, 3072, 12288, 64, 2)
+    assert n > 0 and n % 256 == 0
+    assert n >= 2 * 3072 * 16 * 4  # at least two K slices of fp32 partials
+    assert lb.workspace_size(16, 3072, 12288, 32, 2) == 0    # group smaller than a chunk
+    assert lb.workspace_size(32, 3072, 12288, 64, 2) == 0    # two row blocks
+    assert lb.workspace_size(16, 3072, 12288, 64, 1) == 0    # binary
+    assert lb.workspace_size(16, 3072, 12200, 64, 2) == 0    # K % g != 0: invalid
+    assert lb.workspace_size(16, 3000, 12288, 64, 2) == 0    # N % 16 != 0: invalid
+
+
+def test_gemm_ex_validates_before_the_device():
+    L = lb.lib()
+    A = 256
+    assert L.lowbit_gemm_ex(A, A, A, A, 16, 3072, 3072, 64, 2, A + 8, 1 << 20, None) == ALIGN
+    assert L.lowbit_gemm_ex(None, A, A, A, 16, 3072, 3072, 64, 2, A, 1 << 20, None) == INVALID
+    assert L.lowbit_gemm_ex(A, A, A, A, 16, 3072, 3072, 64, 3, A, 1 << 20, None) == UNSUPPORTED
+    assert L.lowbit_gemm_ex(A, A, A, A, 0, 3072, 3072, 64, 2, None, 0, None) == OK
