@@ -31,30 +31,40 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
-KERNEL_SOURCES = ["binary_bit_gemm_amd/csrc/gemm_tiled.hip", "binary_bit_gemm_amd/csrc/lowbit_device.h"]
+# Source files of each kernel variant (plus the shared headers): the committed HBM counter
+# summary of a workload is used only while the sources of the kernels it runs are unchanged.
+VARIANT_SOURCES = {
+    "tile256x256": ["gemm_tiled.hip"], "tile256x128": ["gemm_tiled.hip"], "tile128x256": ["gemm_tiled.hip"],
+    "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "skinny": ["gemm_skinny.hip"],
+    "ring": ["gemm_ring.hip"],
+}
+COMMON_SOURCES = ["lowbit_device.h", "lowbit_internal.h", "gemm_grouped.hip"]
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(variants) -> str:
     import hashlib
+    files = sorted({f for v in variants for f in VARIANT_SOURCES.get(v, [])} | set(COMMON_SOURCES))
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
+    for rel in files:
+        with open(os.path.join(ROOT, "binary_bit_gemm_amd", "csrc", rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when there is none
-    for this workload or the kernel sources changed since it was taken."""
+def measured_traffic(workload: str, variants):
+    """HBM bytes per launch of the workload's kernels from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy), or
+    None when there is none for this workload or the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_sha") != kernel_source_sha():
+    if rec.get("kernel_sha") != kernel_source_sha(variants):
         return None
     return rec.get("bytes_per_launch")
+
+
 PEAK_HBM_GBS = 8000.0
 METRIC = "lowbit GEMM TFLOP/s and % of bf16 MFMA peak (M=4608, ternary g=64)"
 
@@ -117,9 +127,10 @@ def make_device_inputs(probs, seed):
     return bufs
 
 
-def cpu_baseline(probs, rows, seed):
+def cpu_baseline(probs, rows, seed, unit="TFLOP/s"):
     """The oracle as it stands (unpack, fp64 dequantise, numpy matmul) on the first `rows`
-    rows of X for every distinct shape of the workload, on the host's cores."""
+    rows of X for every distinct shape of the workload, on the host's cores, in the unit of
+    the metric (TFLOP/s of 2*M*N*K, or GB/s of the algorithmic bytes of the sampled GEMMs)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -132,6 +143,7 @@ def cpu_baseline(probs, rows, seed):
     for p in probs:
         seen.setdefault((p.N, p.K, p.bits, p.g), p)
     flops = 0
+    nbytes = 0
     elapsed = 0.0
     for (N, K, bits, g), p in seen.items():
         m = p.M if rows <= 0 else min(rows, p.M)
@@ -142,7 +154,9 @@ def cpu_baseline(probs, rows, seed):
         oracle.gemm_ref_from_words(inp.x, words, inp.scales, K, g, bits)
         elapsed += time.perf_counter() - t0
         flops += 2 * m * N * K
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        nbytes += q.bytes_moved()
+    value = flops / elapsed / 1e12 if unit == "TFLOP/s" else nbytes / elapsed / 1e9
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": (f"all {probs[0].M}" if rows <= 0 else f"first {rows}") +
                       f" rows of X for each of the {len(seen)} distinct (N, K) shapes; "
                       f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s"}
@@ -239,7 +253,8 @@ def main():
     launch_ms = event_ms / launches
     kern_tflops = flops_step / (event_ms * 1e-3) / 1e12
     kern_gbs = bytes_step / (event_ms * 1e-3) / 1e9
-    traffic = measured_traffic(a.workload)
+    variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
+    traffic = measured_traffic(a.workload, variants)
 
     if a.workload == "skinny":
         metric, value, unit = "lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)", \
@@ -251,7 +266,7 @@ def main():
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-    roof.update({"kernel": sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs}),
+    roof.update({"kernel": variants, "kernel_sha": kernel_source_sha(variants),
                  "launches_per_step": launches, "avg_launch_us": round(1e3 * launch_ms, 2),
                  "algorithmic_flop_per_launch": flops_step // launches,
                  "algorithmic_bytes_per_launch": bytes_step // launches})
@@ -270,7 +285,7 @@ def main():
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed)
+        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed, unit)
     print(json.dumps(out), flush=True)
 
 
