@@ -23,11 +23,19 @@ int hip_fail(hipError_t e) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Limits of the kernels' addressing: packed weights (and the smaller scales) are read
+// through 32-bit buffer ranges, an X tile of up to 288 rows likewise, and tile counts are
+// 32-bit.  M and X/Y offsets are 64-bit.
+constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxWeightBytes = (int64_t(1) << 32) - 1;
+constexpr int64_t kMaxOutputs = int64_t(1) << 37;
+constexpr int64_t kMaxCodes = int64_t(1) << 40;
 
 int check_pack_args(const void* codes, const void* W, int64_t N, int64_t K, int bits) {
     if (bits != 1 && bits != 2) return LOWBIT_E_UNSUPPORTED;
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return LOWBIT_E_INVALID;
     if (K % (32 / bits) != 0) return LOWBIT_E_INVALID;
+    if (N * K > kMaxCodes) return LOWBIT_E_UNSUPPORTED;
     if (N * K == 0) return LOWBIT_OK;
     if (codes == nullptr || W == nullptr) return LOWBIT_E_INVALID;
     if (!aligned16(codes) || !aligned16(W)) return LOWBIT_E_ALIGN;
@@ -153,6 +161,7 @@ int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, cons
     if (g != 32 && g != 64 && g != 128) return LOWBIT_E_UNSUPPORTED;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return LOWBIT_E_INVALID;
     if (K % g != 0 || N % 16 != 0) return LOWBIT_E_INVALID;
+    if (K > kMaxK || N * K / 8 * bits > kMaxWeightBytes || M * N > kMaxOutputs) return LOWBIT_E_UNSUPPORTED;
     if (M * N == 0) return LOWBIT_OK;
     if (Y == nullptr) return LOWBIT_E_INVALID;
     if (K > 0 && (X == nullptr || W == nullptr || S == nullptr)) return LOWBIT_E_INVALID;

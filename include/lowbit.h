@@ -36,7 +36,10 @@
  *   - Arguments are validated on the host before anything is enqueued; a non-zero
  *     return means nothing was launched.
  *   - Supported: bits in {1, 2}; g in {32, 64, 128}; K % g == 0; N % 16 == 0; M >= 0
- *     (M == 0 or N == 0 is a no-op); M, N, K < 2^31; the current device is gfx950.
+ *     (M == 0 or N == 0 is a no-op); M, N < 2^31; K <= 2^22; packed weights under 4 GiB
+ *     (N*K*bits/8 < 2^32); M*N <= 2^37; the current device is gfx950.  lowbit_pack and
+ *     lowbit_unpack take N*K <= 2^40 codes.  Shapes past these limits return
+ *     LOWBIT_E_UNSUPPORTED.
  *   - The library allocates no device memory and uses no hidden workspace; the only
  *     workspace is the one a caller passes to lowbit_gemm_ex.
  *   - Results are deterministic: the same inputs give bitwise the same Y on every run.
@@ -57,7 +60,7 @@ extern "C" {
 enum {
     LOWBIT_OK = 0,
     LOWBIT_E_INVALID = 1,     /* null pointer, negative size, N % 16 or K % g != 0 ...     */
-    LOWBIT_E_UNSUPPORTED = 2, /* bits / g outside the supported set, or device not gfx950  */
+    LOWBIT_E_UNSUPPORTED = 2, /* bits / g or a size outside the supported set, or device not gfx950 */
     LOWBIT_E_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned                   */
     LOWBIT_E_HIP = 4,         /* a HIP runtime call failed; see lowbit_last_hip_error()    */
     LOWBIT_E_TOO_MANY = 5     /* batched call: more problems than one call accepts         */

@@ -65,6 +65,13 @@ A = 0x10000  # a 16-byte-aligned fake address: never dereferenced by the host ch
     ((0, 0, 0, A, 64, 256, 0, 64, 2), OK),                    # K == 0: Y = 0, no inputs read
     ((A, A, A, A, 64, 256, 256, 128, 1), OK),
     ((A, A, A, A, 64, 256, 256, 32, 1), OK),
+    ((A, A, A, A, 64, 256, 1 << 22, 64, 2), OK),               # size limits of the kernels' addressing
+    ((A, A, A, A, 64, 256, (1 << 22) + 64, 64, 2), UNSUPPORTED),
+    ((A, A, A, A, 64, (1 << 20) - 16, 1 << 14, 64, 2), OK),    # packed weights 4 GiB - 64 KiB ...
+    ((A, A, A, A, 64, 1 << 20, 1 << 14, 64, 2), UNSUPPORTED),  # ... and exactly 4 GiB
+    ((A, A, A, A, 64, 1 << 21, 1 << 15, 64, 1), UNSUPPORTED),  # binary: 8 GiB
+    ((A, A, A, A, 1 << 30, 1 << 7, 256, 64, 2), OK),           # M*N = 2^37
+    ((A, A, A, A, 1 << 30, 1 << 8, 256, 64, 2), UNSUPPORTED),
 ])
 def test_check_gemm_args(args, want):
     assert lb.check_gemm_args(*args) == want
@@ -78,6 +85,8 @@ def test_gemm_rejects_before_touching_the_device():
     assert st == INVALID
     st = L.lowbit_unpack(A, A, 16, 32, 5, None)
     assert st == UNSUPPORTED
+    assert L.lowbit_pack(A, A, 1 << 21, 1 << 20, 2, None, None) == UNSUPPORTED  # 2^41 codes
+    assert L.lowbit_gemm(A, A, A, A, 64, 1 << 20, 1 << 14, 64, 2, None) == UNSUPPORTED  # 4 GiB of words
     probs = (lb.Problem * 2)()
     probs[0] = lb.Problem(A, A, A, A, 64, 256, 256, 64, 2)
     probs[1] = lb.Problem(A, A, A, A, 64, 256, 256, 64, 7)
