@@ -41,13 +41,26 @@ VARIANT_SOURCES = {
 COMMON_SOURCES = ["lowbit_device.h", "lowbit_internal.h", "gemm_grouped.hip"]
 
 
-def kernel_source_sha(variants) -> str:
+def strip_comments(src: str) -> str:
+    """Source text without comments, trailing blanks and empty lines (the sources hold no
+    string literal with a comment marker in it)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
+def kernel_source_sha(variants, read=None) -> str:
+    """sha256 over the code (comments stripped) of the sources the variants are built from."""
     import hashlib
     files = sorted({f for v in variants for f in VARIANT_SOURCES.get(v, [])} | set(COMMON_SOURCES))
+    if read is None:
+        def read(rel):
+            with open(os.path.join(ROOT, "binary_bit_gemm_amd", "csrc", rel)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for rel in files:
-        with open(os.path.join(ROOT, "binary_bit_gemm_amd", "csrc", rel), "rb") as fh:
-            h.update(fh.read())
+        h.update(strip_comments(read(rel)).encode())
     return h.hexdigest()
 
 
@@ -80,6 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of X in the CPU oracle sample (0 = all rows of the workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle sample until it has run this long")
     ap.add_argument("--graph", action="store_true",
                     help="launch each step as one captured HIP graph (measured slightly slower than eager launches "
                          "on these workloads, so off by default)")
@@ -127,7 +142,7 @@ def make_device_inputs(probs, seed):
     return bufs
 
 
-def cpu_baseline(probs, rows, seed, unit="TFLOP/s"):
+def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0):
     """The oracle as it stands (unpack, fp64 dequantise, numpy matmul) on the first `rows`
     rows of X for every distinct shape of the workload, on the host's cores, in the unit of
     the metric (TFLOP/s of 2*M*N*K, or GB/s of the algorithmic bytes of the sampled GEMMs)."""
@@ -142,23 +157,28 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s"):
     seen = {}
     for p in probs:
         seen.setdefault((p.N, p.K, p.bits, p.g), p)
-    flops = 0
-    nbytes = 0
-    elapsed = 0.0
+    cases = []
     for (N, K, bits, g), p in seen.items():
         m = p.M if rows <= 0 else min(rows, p.M)
         q = W.Problem(p.name, m, N, K, bits, g, p.config_id, p.tensor_id)
         inp = W.make_inputs(q, seed)
         words, _ = oracle.pack(inp.codes, bits)
-        t0 = time.perf_counter()
-        oracle.gemm_ref_from_words(inp.x, words, inp.scales, K, g, bits)
-        elapsed += time.perf_counter() - t0
-        flops += 2 * m * N * K
-        nbytes += q.bytes_moved()
+        cases.append((q, inp, words))
+    # whole passes over the sample until at least `min_seconds` of oracle time
+    flops = nbytes = passes = 0
+    elapsed = 0.0
+    while passes == 0 or elapsed < min_seconds:
+        for q, inp, words in cases:
+            t0 = time.perf_counter()
+            oracle.gemm_ref_from_words(inp.x, words, inp.scales, q.K, q.g, q.bits)
+            elapsed += time.perf_counter() - t0
+            flops += 2 * q.M * q.N * q.K
+            nbytes += q.bytes_moved()
+        passes += 1
     value = flops / elapsed / 1e12 if unit == "TFLOP/s" else nbytes / elapsed / 1e9
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": (f"all {probs[0].M}" if rows <= 0 else f"first {rows}") +
-                      f" rows of X for each of the {len(seen)} distinct (N, K) shapes; "
+                      f" rows of X for each of the {len(seen)} distinct (N, K) shapes, {passes} passes; "
                       f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s"}
 
 
@@ -285,7 +305,7 @@ def main():
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed, unit)
+        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed, unit, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

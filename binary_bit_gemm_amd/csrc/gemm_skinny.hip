@@ -4,10 +4,12 @@
 // to a bf16 operand once and meets only M activations.  Each workgroup owns a stripe of NCB
 // column blocks of 16 output columns and its waves split K into contiguous step ranges.  The
 // partial sums of the waves are combined in LDS in a fixed order (wave 0 first), so the
-// result does not depend on timing.  Nothing goes through LDS on the way in:
+// result does not depend on timing.  On the way in:
 //   * packed weights stream from HBM straight into registers, 16 bytes per lane per column
 //     block and step (one 64-byte piece of each of the block's 16 weight rows);
-//   * activations come from L2 (X is a few hundred KB at most), 16 bytes per lane per MFMA;
+//   * activations (a few hundred KB at most, so L2-resident) are copied per wave and step
+//     into LDS for ternary codes and M <= 16, and loaded straight into registers, 16 bytes
+//     per lane per MFMA, otherwise;
 //   * one step of both is in flight while the previous step is computed.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16, A = 16 activation rows x 32 K, B = 32 K x 16 weight rows.
