@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 VARIANT_SOURCES = {
     "tile256x256": ["gemm_tiled.hip"], "tile256x128": ["gemm_tiled.hip"], "tile128x256": ["gemm_tiled.hip"],
     "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "skinny": ["gemm_skinny.hip"],
-    "ring": ["gemm_ring.hip"],
+    "resident": ["gemm_resident.hip"],
 }
 COMMON_SOURCES = ["lowbit_device.h", "lowbit_internal.h", "gemm_grouped.hip"]
 
@@ -205,12 +205,23 @@ def main():
     groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
     bufs = make_device_inputs(probs, a.seed)
 
+    # one caller workspace (zero-filled once, reused by every call: each call leaves its
+    # counters at zero) for the calls that split K across workgroups
+    need = 0
+    for grp in groups:
+        if len(grp) == 1:
+            p = probs[grp[0]]
+            need = max(need, lb.workspace_size(p.M, p.N, p.K, p.g, p.bits))
+        else:
+            need = max(need, lb.batched_workspace_size([bufs[i] for i in grp]))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need > 0 else None
+
     def launch(grp):
         if len(grp) == 1:
             x, w, s, y, g, bits = bufs[grp[0]]
-            lb.gemm(x, w, s, g, bits, out=y)
+            lb.gemm(x, w, s, g, bits, out=y, workspace=ws)
         else:
-            lb.gemm_batched([bufs[i] for i in grp])
+            lb.gemm_batched([bufs[i] for i in grp], workspace=ws)
 
     def step():
         for grp in groups:
@@ -295,6 +306,7 @@ def main():
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "gemms_per_step": len(probs), "launches_per_step": launches,
+                   "workspace_bytes": need,
                    "graph": graph is not None,
                    "shapes": sorted({f"{p.M}x{p.N}x{p.K}" for p in probs}),
                    "bits": sorted({p.bits for p in probs}), "g": sorted({p.g for p in probs}),

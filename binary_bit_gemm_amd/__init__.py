@@ -140,9 +140,7 @@ class Problem(ctypes.Structure):
                 ("g", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
-def gemm_batched(problems: Sequence[Tuple["object", "object", "object", "object", int, int]]) -> None:
-    """Run independent GEMMs [(x, words, scales, out, g, bits), ...] as grouped launches.
-    Outputs are written in place; all tensors on the same device."""
+def _problem_array(problems):
     torch = _torch()
     if len(problems) > MAX_BATCH:
         raise ValueError(f"at most {MAX_BATCH} problems per call")
@@ -159,10 +157,33 @@ def gemm_batched(problems: Sequence[Tuple["object", "object", "object", "object"
             raise ValueError(f"problem {i}: inconsistent shapes")
         dev = x.device
         arr[i] = Problem(x.data_ptr(), w.data_ptr(), s.data_ptr(), y.data_ptr(), M, N, K, g, bits)
+    return arr, dev
+
+
+def batched_workspace_size(problems: Sequence[Tuple["object", "object", "object", "object", int, int]]) -> int:
+    """Bytes of workspace gemm_batched(..., workspace=...) can use (0: none needed)."""
+    arr, _ = _problem_array(problems)
+    return int(lib().lowbit_batched_workspace_size(arr, len(problems))) if problems else 0
+
+
+def gemm_batched(problems: Sequence[Tuple["object", "object", "object", "object", int, int]],
+                 workspace=None) -> None:
+    """Run independent GEMMs [(x, words, scales, out, g, bits), ...] as grouped launches.
+    Outputs are written in place; all tensors on the same device.  `workspace`: as for gemm()
+    (size from batched_workspace_size)."""
+    arr, dev = _problem_array(problems)
     if not problems:
         return
-    st = lib().lowbit_gemm_batched(arr, len(problems), ctypes.c_void_p(_stream_ptr(dev)))
-    _check(st, "lowbit_gemm_batched")
+    stream = ctypes.c_void_p(_stream_ptr(dev))
+    if workspace is None:
+        st = lib().lowbit_gemm_batched(arr, len(problems), stream)
+        _check(st, "lowbit_gemm_batched")
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        st = lib().lowbit_gemm_batched_ex(arr, len(problems), ctypes.c_void_p(workspace.data_ptr()),
+                                          workspace.numel() * workspace.element_size(), stream)
+        _check(st, "lowbit_gemm_batched_ex")
 
 
 def check_gemm_args(x_ptr: int, w_ptr: int, s_ptr: int, y_ptr: int, M: int, N: int, K: int, g: int,

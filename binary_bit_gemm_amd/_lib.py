@@ -17,6 +17,8 @@ SIGNATURES = {
     "lowbit_gemm_batched": (_INT, [_VP, _INT, _VP]),
     "lowbit_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _INT, _INT]),
     "lowbit_gemm_ex": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP, ctypes.c_size_t, _VP]),
+    "lowbit_batched_workspace_size": (ctypes.c_size_t, [_VP, _INT]),
+    "lowbit_gemm_batched_ex": (_INT, [_VP, _INT, _VP, ctypes.c_size_t, _VP]),
     "lowbit_check_gemm_args": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT]),
     "lowbit_gemm_variant": (ctypes.c_char_p, [_I64, _I64, _I64, _INT, _INT]),
     "lowbit_status_string": (ctypes.c_char_p, [_INT]),

@@ -42,17 +42,6 @@ struct SkinnyFmt {
     static constexpr int XPS = 4 * MPC;             // activation operands per step and row block
 };
 
-// Lane quarter q of register c ends up holding word q of chunk c (see the file comment).
-__device__ __forceinline__ void transpose_words(u32x4_t& w) {
-    uint32_t r0 = w[0], r1 = w[1], r2 = w[2], r3 = w[3];
-    auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-    auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-    r0 = a[0]; r2 = a[1]; r1 = b[0]; r3 = b[1];
-    auto c = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
-    auto d = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
-    w = u32x4_t{c[0], c[1], d[0], d[1]};
-}
-
 template <int BITS, int G, int MB, int NCB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup grp) {
     using F = SkinnyFmt<BITS>;

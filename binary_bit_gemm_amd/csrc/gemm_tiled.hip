@@ -375,8 +375,6 @@ constexpr TileShape kTiles[] = {
     {TILE_64x256, 64, 256, 2, 0.75f},
 };
 
-constexpr int kComputeUnits = 256;
-
 }  // namespace
 
 int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {

@@ -55,8 +55,8 @@ int device_check() {
     return r == 1 ? LOWBIT_OK : LOWBIT_E_UNSUPPORTED;
 }
 
-// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | tile256 | tile256w | tile128 | tile64 |
-// tile288 (the last falls back to tile256w where the 16x16 kernel does not apply)
+// Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | resident | tile256 | tile256w |
+// tile128 | tile64 | tile288 (the last falls back to tile256w where the 16x16 kernel does not apply)
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
@@ -66,30 +66,26 @@ int forced_variant() {
     if (std::strcmp(v, "tile128") == 0) return lowbit::TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return lowbit::TILE_64x256;
     if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
-    if (std::strcmp(v, "ring") == 0) return 101;
+    if (std::strcmp(v, "resident") == 0) return 102;
     return -1;
 }
 
-// Largest K split of the ring kernel (LOWBIT_RING_MAX_SPLITS, for A/B runs and tests).
-int ring_max_splits() {
-    const char* v = std::getenv("LOWBIT_RING_MAX_SPLITS");
-    const int n = v != nullptr ? std::atoi(v) : 0;
-    return n >= 1 && n <= 64 ? n : 16;
-}
-
-// Ring kernel without a workspace: only when it fills the machine without splitting K.
-bool ring_without_workspace(int64_t M, int64_t N, int64_t K, int g, int bits) {
-    if (!lowbit::ring_supported(M, N, K, g, bits)) return false;
-    const lowbit::RingPlan plan = lowbit::plan_ring(N, K, 1);
-    return plan.tiles * plan.splits >= 384;
+// Resident plan of one problem (len 0: not covered).  `may_split`: a workspace is available.
+lowbit::ResidentPlan resident_plan(int64_t M, int64_t N, int64_t K, int g, int bits, bool may_split) {
+    if (!lowbit::resident_supported(M, N, K, g, bits)) return lowbit::ResidentPlan{};
+    const lowbit::GemmProblem p{nullptr, nullptr, nullptr, nullptr, int(M), int(N), int(K)};
+    return lowbit::plan_resident(&p, 1, g, may_split);
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     const int f = forced_variant();
-    if (f == 101 && lowbit::ring_supported(M, N, K, g, bits)) return 101;
+    if (f == 102 && resident_plan(M, N, K, g, bits, false).len > 0) return 102;
     if (f == 100 && lowbit::use_skinny(M, N, K, g, bits)) return 100;
-    if (f >= 0 && f != 100 && f != 101) return f;
-    if (ring_without_workspace(M, N, K, g, bits)) return 101;
+    if (f >= 0 && f < 100) return f;
+    if (f < 0 && lowbit::resident_supported(M, N, K, g, bits)) {
+        const lowbit::GemmProblem p{nullptr, nullptr, nullptr, nullptr, int(M), int(N), int(K)};
+        if (lowbit::resident_preferred(&p, 1, g, false)) return 102;
+    }
     if (lowbit::use_skinny(M, N, K, g, bits)) return 100;
     return lowbit::pick_tile_variant(M, N, K, g, bits);
 }
@@ -108,14 +104,62 @@ int launch_one(const lowbit::GemmProblem& p, int g, int bits, hipStream_t stream
         e = hipGetLastError();
     } else {
         const int v = choose_variant(p.M, p.N, p.K, g, bits);
-        if (v == 101) {
-            e = lowbit::launch_gemm_ring(p, g, lowbit::plan_ring(p.N, p.K, 1), nullptr, stream);
+        if (v == 102) {
+            e = lowbit::launch_gemm_resident_group(&p, 1, g, lowbit::plan_resident(&p, 1, g, false), nullptr, stream);
         } else {
             e = v == 100 ? lowbit::launch_gemm_skinny(p, g, bits, stream)
                          : lowbit::launch_gemm_tiled(p, g, bits, v, stream);
         }
     }
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
+// Calls f(group, n, g, bits) for the problems of each (g, bits) class with M, N, K > 0.
+template <class F>
+int for_each_class(const lowbit_problem* problems, int count, F&& f) {
+    static const int kClasses[6][2] = {{64, 2}, {64, 1}, {128, 2}, {128, 1}, {32, 2}, {32, 1}};
+    lowbit::GemmProblem grp[LOWBIT_MAX_BATCH];
+    for (const auto& cls : kClasses) {
+        int n = 0;
+        for (int i = 0; i < count; ++i) {
+            const lowbit_problem& q = problems[i];
+            if (q.g != cls[0] || q.bits != cls[1] || q.M * q.N == 0 || q.K == 0) continue;
+            grp[n++] = lowbit::GemmProblem{static_cast<const uint16_t*>(q.X), q.W, static_cast<const uint16_t*>(q.S),
+                                           static_cast<uint16_t*>(q.Y), int(q.M), int(q.N), int(q.K)};
+        }
+        if (n == 0) continue;
+        const int st = f(grp, n, cls[0], cls[1]);
+        if (st != LOWBIT_OK) return st;
+    }
+    return LOWBIT_OK;
+}
+
+int batched(const lowbit_problem* problems, int count, void* workspace, size_t workspace_bytes, void* stream) {
+    if (count < 0 || (count > 0 && problems == nullptr)) return LOWBIT_E_INVALID;
+    if (count > LOWBIT_MAX_BATCH) return LOWBIT_E_TOO_MANY;
+    for (int i = 0; i < count; ++i) {
+        const lowbit_problem& q = problems[i];
+        const int st = lowbit_check_gemm_args(q.X, q.W, q.S, q.Y, q.M, q.N, q.K, q.g, q.bits);
+        if (st != LOWBIT_OK) return st;
+    }
+    if (count == 0) return LOWBIT_OK;
+    int st = device_check();
+    if (st != LOWBIT_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // K == 0: Y = 0
+    for (int i = 0; i < count; ++i) {
+        const lowbit_problem& q = problems[i];
+        if (q.M * q.N == 0 || q.K != 0) continue;
+        lowbit::GemmProblem p{static_cast<const uint16_t*>(q.X), q.W, static_cast<const uint16_t*>(q.S),
+                              static_cast<uint16_t*>(q.Y), int(q.M), int(q.N), int(q.K)};
+        st = launch_one(p, q.g, q.bits, s);
+        if (st != LOWBIT_OK) return st;
+    }
+    // each (g, bits) class: one grouped launch per kernel family
+    return for_each_class(problems, count, [&](const lowbit::GemmProblem* grp, int n, int g, int bits) {
+        const hipError_t e = lowbit::launch_gemm_grouped(grp, n, g, bits, workspace, workspace_bytes, s);
+        return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+    });
 }
 
 }  // namespace
@@ -173,7 +217,7 @@ int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, cons
 const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits) {
     int v = choose_variant(M, N, K, g, bits);
     if (v == 100) return "skinny";
-    if (v == 101) return "ring";
+    if (v == 102) return "resident";
     if (v == lowbit::TILE_288x192 && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
     return lowbit::tile_variant_name(v);
 }
@@ -210,8 +254,9 @@ int lowbit_gemm(const void* X, const uint32_t* W, const void* S, void* Y,
 
 size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits) {
     if (lowbit_check_gemm_args(nullptr, nullptr, nullptr, nullptr, 0, N, K, g, bits) != LOWBIT_OK) return 0;
-    if (!lowbit::ring_supported(M, N, K, g, bits)) return 0;
-    return lowbit::ring_workspace_bytes(lowbit::plan_ring(N, K, ring_max_splits()), N);
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const lowbit::GemmProblem p{nullptr, nullptr, nullptr, nullptr, int(M), int(N), int(K)};
+    return lowbit::grouped_workspace_bytes(&p, 1, g, bits);
 }
 
 int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y, int64_t M, int64_t N, int64_t K,
@@ -219,54 +264,37 @@ int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y, int
     int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);
     if (st != LOWBIT_OK || M * N == 0) return st;
     if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
-    if (K == 0 || !lowbit::ring_supported(M, N, K, g, bits) || forced_variant() >= 0)
-        return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
-    const lowbit::RingPlan plan = lowbit::plan_ring(N, K, ring_max_splits());
-    if (plan.splits > 1 && (workspace == nullptr || workspace_bytes < lowbit::ring_workspace_bytes(plan, N)))
+    const size_t need = lowbit_workspace_size(M, N, K, g, bits);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need || forced_variant() >= 0)
         return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
     st = device_check();
     if (st != LOWBIT_OK) return st;
     lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
                           static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
-    const hipError_t e = lowbit::launch_gemm_ring(p, g, plan, workspace, static_cast<hipStream_t>(stream));
+    const hipError_t e = lowbit::launch_gemm_grouped(&p, 1, g, bits, workspace, workspace_bytes,
+                                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 
-int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream) {
-    if (count < 0 || (count > 0 && problems == nullptr)) return LOWBIT_E_INVALID;
-    if (count > LOWBIT_MAX_BATCH) return LOWBIT_E_TOO_MANY;
-    for (int i = 0; i < count; ++i) {
-        const lowbit_problem& q = problems[i];
-        const int st = lowbit_check_gemm_args(q.X, q.W, q.S, q.Y, q.M, q.N, q.K, q.g, q.bits);
-        if (st != LOWBIT_OK) return st;
-    }
-    if (count == 0) return LOWBIT_OK;
-    int st = device_check();
-    if (st != LOWBIT_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+size_t lowbit_batched_workspace_size(const lowbit_problem* problems, int count) {
+    if (count <= 0 || count > LOWBIT_MAX_BATCH || problems == nullptr) return 0;
+    size_t need = 0;
+    for_each_class(problems, count, [&](const lowbit::GemmProblem* grp, int n, int g, int bits) {
+        const size_t b = lowbit::grouped_workspace_bytes(grp, n, g, bits);
+        need = b > need ? b : need;
+        return LOWBIT_OK;
+    });
+    return need;
+}
 
-    // Problems of one (g, bits) class with K > 0 go into one grouped launch.
-    static const int kClasses[6][2] = {{64, 2}, {64, 1}, {128, 2}, {128, 1}, {32, 2}, {32, 1}};
-    lowbit::GemmProblem grp[LOWBIT_MAX_BATCH];
-    for (const auto& cls : kClasses) {
-        int n = 0;
-        for (int i = 0; i < count; ++i) {
-            const lowbit_problem& q = problems[i];
-            if (q.g != cls[0] || q.bits != cls[1] || q.M * q.N == 0) continue;
-            lowbit::GemmProblem p{static_cast<const uint16_t*>(q.X), q.W, static_cast<const uint16_t*>(q.S),
-                                  static_cast<uint16_t*>(q.Y), int(q.M), int(q.N), int(q.K)};
-            if (q.K == 0) {
-                st = launch_one(p, q.g, q.bits, s);
-                if (st != LOWBIT_OK) return st;
-                continue;
-            }
-            grp[n++] = p;
-        }
-        if (n == 0) continue;
-        hipError_t e = lowbit::launch_gemm_grouped(grp, n, cls[0], cls[1], s);
-        if (e != hipSuccess) return hip_fail(e);
-    }
-    return LOWBIT_OK;
+int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
+    return batched(problems, count, forced_variant() >= 0 ? nullptr : workspace, workspace_bytes, stream);
+}
+
+int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream) {
+    return batched(problems, count, nullptr, 0, stream);
 }
 
 }  // extern "C"

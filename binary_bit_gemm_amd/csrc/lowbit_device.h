@@ -104,6 +104,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
+// 4x4 transpose of (lane quarter, register) blocks: lane quarter q (lanes 16q .. 16q+15)
+// holds words w[0..3] of its 16-byte piece q; afterwards register c of lane quarter q holds
+// word q of piece c.  Four lane-row swaps (v_permlane32_swap, v_permlane16_swap).
+__device__ __forceinline__ void transpose_words(u32x4_t& w) {
+    uint32_t r0 = w[0], r1 = w[1], r2 = w[2], r3 = w[3];
+    auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    r0 = a[0]; r2 = a[1]; r1 = b[0]; r3 = b[1];
+    auto c = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
+    w = u32x4_t{c[0], c[1], d[0], d[1]};
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone).  Vector-memory operations complete
+// in issue order, so vmcnt(N) means "all but the last N issued are done".
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // encoding: vmcnt in bits [3:0] and [15:14], expcnt 7, lgkmcnt 15
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS that keeps loads in flight.  __syncthreads() releases at
+// workgroup scope, which on gfx9 waits for every outstanding vector-memory operation --
+// prefetches included.  Where each wave has already waited (counted waits) for its own
+// copies into LDS, a bare s_barrier is enough; the empty asm statements keep the compiler
+// from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // 16-byte direct-to-LDS copy: lane i's 16 bytes (at voff + soff in the buffer) land at
 // lds_wave_base + 16 * i.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff, int soff) {

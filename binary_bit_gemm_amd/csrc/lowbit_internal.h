@@ -19,6 +19,7 @@ struct GemmProblem {
 // launch belongs to the first problem i with w < tile_end[i] (inclusive prefix sums of the
 // per-problem workgroup counts) and works on its local tile w - tile_end[i - 1].
 constexpr int kMaxGroup = 16;
+constexpr int kComputeUnits = 256;  // MI355X
 struct ProblemGroup {
     GemmProblem p[kMaxGroup];
     int tile_end[kMaxGroup];
@@ -42,28 +43,29 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant,
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream);
 bool skinny_supported(int g, int bits);
 
-// Ring kernel (ternary, M <= 16, g = 64 / 128, K % 256 == 0, N % 64 == 0): deep LDS load
-// ring, optional split-K across workgroups through a caller-provided workspace.
-struct RingArgs {
-    GemmProblem p;
-    int splits;           // workgroups per column tile along K
-    float* ws;            // fp32 partial sums (splits > 1)
-    uint32_t* counters;   // one arrival counter per column tile, zero between calls
+// Resident kernel (ternary, M <= 16, g = 64 / 128, K % 256 == 0): the activations of a
+// workgroup's K range in LDS, each wave issues every weight load of its (column block, K
+// slice) at once; optionally split along K across workgroups through a caller workspace.
+// One launch per group of problems with the same K.
+struct ResidentPlan {
+    int cb;      // column blocks per workgroup
+    int ks;      // K slices per column block inside a workgroup (waves = cb * ks)
+    int len;     // most steps of one wave; 0 = shape not covered
+    int splits;  // workgroups per column group along K (> 1 needs the workspace)
+    int tiles;   // column groups of the launch
 };
-struct RingPlan {
-    int nw;      // 16-column blocks per wave (a column tile is 4 * nw blocks)
-    int splits;  // workgroups per column tile along K
-    int tiles;   // column tiles
-};
-bool ring_supported(int64_t M, int64_t N, int64_t K, int g, int bits);
-RingPlan plan_ring(int64_t N, int64_t K, int max_splits);
-size_t ring_workspace_bytes(const RingPlan& plan, int64_t N);
-hipError_t launch_gemm_ring(const GemmProblem& p, int g, const RingPlan& plan, void* workspace, hipStream_t stream);
+bool resident_supported(int64_t M, int64_t N, int64_t K, int g, int bits);
+ResidentPlan plan_resident(const GemmProblem* probs, int count, int g, bool may_split);
+size_t resident_workspace_bytes(const ResidentPlan& plan);
+bool resident_preferred(const GemmProblem* probs, int count, int g, bool may_split);
+hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g, const ResidentPlan& plan,
+                                      void* workspace, hipStream_t stream);
 
 // Grouped launch: problems of one (g, bits) class; one launch per kernel family and per
 // kMaxGroup problems.
-hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int bits,
-                               hipStream_t stream);
+hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int bits, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t grouped_workspace_bytes(const GemmProblem* probs, int count, int g, int bits);
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream);
 hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);

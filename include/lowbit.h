@@ -120,10 +120,12 @@ int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream)
 /*
  * lowbit_workspace_size -- bytes of caller-provided device workspace with which
  * lowbit_gemm_ex can split K across workgroups for this shape (0: it never needs one).
- * The split applies to skinny ternary problems (M <= 16, g = 64 or 128, K % 256 == 0,
- * N % 64 == 0); there the fp32 partial sums of the K slices are added in a fixed order, so
- * the result is deterministic (it can differ in the last bits from lowbit_gemm's, which
- * splits K differently).  Returns 0 for invalid arguments.
+ * The split applies to skinny ternary problems (M <= 16, g = 64 or 128, K % 256 == 0)
+ * whose K is too long for the activations of the whole K to stay in one workgroup's LDS
+ * (K above about 4.5K).  The fp32
+ * partial sums of the K ranges are added in a fixed order, so the result is deterministic
+ * (it can differ in the last bits from lowbit_gemm's, which splits K differently).
+ * Returns 0 for invalid arguments.
  */
 size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits);
 
@@ -139,6 +141,16 @@ size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits);
 int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y,
                    int64_t M, int64_t N, int64_t K, int g, int bits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lowbit_batched_workspace_size / lowbit_gemm_batched_ex -- lowbit_gemm_batched with a
+ * caller-provided workspace, under the same rules as lowbit_gemm_ex: the launches of one
+ * call use the workspace one after the other on `stream`; size from
+ * lowbit_batched_workspace_size (0 for invalid arguments or when no launch needs one).
+ */
+size_t lowbit_batched_workspace_size(const lowbit_problem* problems, int count);
+int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */

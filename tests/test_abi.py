@@ -123,22 +123,36 @@ def test_skinny_variant_choice():
     assert lb.variant(17, 3072, 3072, 128, 1) == "tile64x256"
 
 
-def test_ring_variant_and_workspace_size():
-    """The ring kernel takes M <= 16 ternary g = 64 / 128 problems; without a workspace only
-    when it fills the machine unsplit (N = 27648: 432 workgroups).  Its split-K workspace is
-    sized on the host: arrival counters + fp32 partials of 16 rows per split."""
-    assert lb.variant(16, 27648, 3072, 64, 2) == "ring"
-    assert lb.variant(16, 27648, 3072, 128, 2) == "ring"
+def test_resident_variant_and_workspace_size():
+    """The resident kernel takes M <= 16 ternary g = 64 / 128 problems; without a workspace
+    from 512 column blocks up (N = 27648), whole K.  With a workspace, problems whose K is too
+    long for the activations to stay in LDS split K across workgroups: arrival counters +
+    fp32 partials of 16 x 16 outputs per column block and K range."""
+    assert lb.variant(16, 27648, 3072, 64, 2) == "resident"
+    assert lb.variant(16, 27648, 3072, 128, 2) == "resident"
+    assert lb.variant(16, 9216, 3072, 64, 2) == "resident"
+    assert lb.variant(16, 3072, 3072, 64, 2) == "skinny"
     assert lb.variant(17, 27648, 3072, 64, 2) == "skinny"
     assert lb.variant(16, 27648, 3072, 128, 1) == "skinny"
+    assert lb.workspace_size(16, 27648, 3072, 64, 2) == 0     # whole K
     n = lb.workspace_size(16, 3072, 12288, 64, 2)
     assert n > 0 and n % 256 == 0
-    assert n >= 2 * 3072 * 16 * 4  # at least two K slices of fp32 partials
-    assert lb.workspace_size(16, 3072, 12288, 32, 2) == 0    # group smaller than a chunk
-    assert lb.workspace_size(32, 3072, 12288, 64, 2) == 0    # two row blocks
-    assert lb.workspace_size(16, 3072, 12288, 64, 1) == 0    # binary
-    assert lb.workspace_size(16, 3072, 12200, 64, 2) == 0    # K % g != 0: invalid
-    assert lb.workspace_size(16, 3000, 12288, 64, 2) == 0    # N % 16 != 0: invalid
+    assert n >= 2 * 3072 * 16 * 4                             # at least two K ranges of partials
+    assert lb.workspace_size(16, 3072, 3072, 64, 2) == 0      # the whole K fits: no split
+    assert lb.workspace_size(16, 512, 6144, 128, 2) > 0       # 24 steps of activations do not
+    assert lb.workspace_size(16, 3072, 12288, 32, 2) == 0     # group smaller than a piece
+    assert lb.workspace_size(32, 3072, 12288, 64, 2) == 0     # two row blocks
+    assert lb.workspace_size(16, 3072, 12288, 64, 1) == 0     # binary
+    assert lb.workspace_size(16, 3072, 12200, 64, 2) == 0     # K % g != 0: invalid
+    assert lb.workspace_size(16, 3000, 12288, 64, 2) == 0     # N % 16 != 0: invalid
+    L = lb.lib()
+    probs = (lb.Problem * 2)()
+    probs[0] = lb.Problem(A, A, A, A, 16, 3072, 9216, 64, 2)
+    probs[1] = lb.Problem(A, A, A, A, 16, 3072, 9216, 64, 2)
+    assert L.lowbit_batched_workspace_size(probs, 2) > 0     # K-heavy pair: split
+    probs[0] = lb.Problem(A, A, A, A, 16, 18432, 3072, 64, 2)
+    probs[1] = lb.Problem(A, A, A, A, 16, 18432, 3072, 64, 2)
+    assert L.lowbit_batched_workspace_size(probs, 2) == 0    # wide pair: whole K
 
 
 def test_gemm_ex_validates_before_the_device():
