@@ -289,17 +289,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
         compute(xa0, ops);
     }
 
-    // ---- epilogue: 16x16 block layout: lane holds column lane % 16, rows 4 * (lane / 16) + i ----
+    // ---- epilogue ----
+    // 16x16 block layout: lane (q, l16) holds column l16, rows 4q + i.  A 4x4 transpose inside
+    // each group of four lanes l16 = 4a + b (two DPP quad permutes and byte permutes of bf16
+    // pairs) gives lane (q, 4a + b) row 4q + b, columns 4a .. 4a + 3: one 8-byte store instead
+    // of four 2-byte ones.
+    //   stage 1, lanes b <-> b ^ 2: lanes b < 2 keep rows (0, 1) of their column and take rows
+    //            (0, 1) of column b + 2; lanes b >= 2 keep rows (2, 3) and take column b - 2's.
+    //            E = column b & 1, F = column (b & 1) + 2, both for the lane's row pair.
+    //   stage 2, lanes b <-> b ^ 1: even lanes keep the first row of the pair, odd lanes the
+    //            second; each sends the partner the halves it needs.
+    const int b4 = l16 & 3;
+    const bool lower_pair = b4 < 2, odd = (b4 & 1) != 0;
+    const uint32_t send_sel = odd ? 0x05040100u : 0x07060302u;   // (E.lo, F.lo) : (E.hi, F.hi)
+    const uint32_t d0_sel = odd ? 0x03020504u : 0x05040100u;     // (R.lo, E.hi) : (E.lo, R.lo)
+    const uint32_t d1_sel = odd ? 0x03020706u : 0x07060100u;     // (R.hi, F.hi) : (F.lo, R.hi)
+    constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+    constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+    auto pack = [](float lo, float hi) {
+        return uint32_t(float_to_bf16_bits(lo)) | (uint32_t(float_to_bf16_bits(hi)) << 16);
+    };
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-            const int n = n0 + wn0 + nb * 16 + l16;
-            if (n >= N) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm0 + mb * 16 + 4 * q + i;
-                if (m < M) p.Y[int64_t(m) * N + n] = float_to_bf16_bits(acc[mb][nb][i]);
+            const int nblk = n0 + wn0 + nb * 16;
+            if (nblk >= N) continue;  // N % 16 == 0: a block is in or out as a whole
+            const uint32_t P = pack(acc[mb][nb][0], acc[mb][nb][1]);  // rows 0, 1 of column b4
+            const uint32_t Q = pack(acc[mb][nb][2], acc[mb][nb][3]);  // rows 2, 3
+            const uint32_t own = lower_pair ? P : Q;
+            const uint32_t got = uint32_t(
+                __builtin_amdgcn_update_dpp(0, int(lower_pair ? Q : P), kQuadSwap2, 0xF, 0xF, true));
+            const uint32_t E = lower_pair ? own : got, F = lower_pair ? got : own;
+            const uint32_t R = uint32_t(
+                __builtin_amdgcn_update_dpp(0, int(perm_b32(F, E, send_sel)), kQuadSwap1, 0xF, 0xF, true));
+            const uint32_t d0 = perm_b32(R, E, d0_sel), d1 = perm_b32(R, F, d1_sel);
+            const int m = m0 + wm0 + mb * 16 + 4 * q + b4;
+            if (m < M) {
+                typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+                *reinterpret_cast<u32x2_t*>(p.Y + int64_t(m) * N + nblk + (l16 & ~3)) = u32x2_t{d0, d1};
             }
         }
     }
