@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
-                    choices=["res1024", "res512", "res512_binary", "sweep", "skinny"])
+                    choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -111,6 +111,8 @@ def problems_for(workload):
         return W.RES512_TERNARY
     if workload == "res512_binary":
         return W.RES512_BINARY
+    if workload == "res1024_binary":
+        return W.RES1024_BINARY_G128
     if workload == "sweep":
         return W.denoise_step_sweep()
     if workload == "skinny":

@@ -31,7 +31,6 @@
 namespace lowbit {
 namespace {
 
-typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 template <int BITS>
 struct SkinnyFmt {

@@ -1,5 +1,5 @@
-// Packed ternary GEMM on 16x16x32 MFMA blocks: Y[M,N] = X[M,K] . dequant(W)[N,K]^T, for scale
-// groups of 64 or 128.
+// Packed ternary or binary GEMM on 16x16x32 MFMA blocks: Y[M,N] = X[M,K] . dequant(W)[N,K]^T,
+// for scale groups of 64 or 128.
 //
 // Why a second tile kernel: with 32x32 blocks a workgroup tile is a multiple of 32 in both
 // directions and 8 waves want a multiple of 8 blocks, so 4608 x 3072 outputs come out as 216
@@ -9,13 +9,21 @@
 // operand bytes, the same code expansion and the same scale FMAs as the 32x32x16 one.
 //
 // Data movement is that of the 32x32 kernel (direct-to-LDS copies of X per 64-element step,
-// of packed weights in 64-byte row blocks = 4 steps, of scales in 8-group blocks; everything
-// double-buffered and XOR-swizzled in 16-byte chunks).  K order inside a step: lane quarter q
-// of a 16x16x32 block takes word q of each weight row's 16-byte step chunk (codes 16q..16q+15
-// of the step) and, in the two MFMAs of the step, its first and second eight codes; the
-// activation operand of quarter q is therefore chunk 2q + j of the row's 128-byte step.  A
-// step is one scale group of 64 (or half of a group of 128, whose scale then multiplies each
-// half: w = scale_g * b, model card "Binary Weight Representation: 1-bit g128").
+// of packed weights in 64-byte row blocks, of scales in 8-group blocks; everything
+// double-buffered and XOR-swizzled in 16-byte chunks).  A step is one scale group of 64 (or
+// half of a group of 128, whose scale then multiplies each half: w = scale_g * b, model card
+// "Binary Weight Representation: 1-bit g128").  A 64-byte weight block holds 4 ternary or 8
+// binary steps of a row.
+//
+// K order inside a step, chosen for gfx950's LDS: a 16-byte read (ds_read_b128) runs at full
+// rate only if lanes l and l + 16 read the same 32-byte block (equal 16-byte chunks, or chunks
+// that differ in bit 0); chunks two or four apart cost a second pass (measured with the LDS
+// bank-conflict counter).  So in MFMA j of a step, lane quarter q takes the eight codes of
+// chunk phi(q, j) = 4 (q >> 1) + (q & 1) + 2 j of the step, and quarters 0/1 and 2/3 read
+// neighbouring chunks of each activation row.  Its codes are then the low (q even) or high
+// (q odd) halves of two consecutive ternary words (codes 32 (q >> 1) + 16 i + 8 (q & 1) ..),
+// or bytes (q & 1) and (q & 1) + 2 of binary word q >> 1; one 8-byte read of the row's step
+// words and one byte permute gather them.
 #include "lowbit_device.h"
 #include "lowbit_internal.h"
 
@@ -25,19 +33,18 @@ namespace {
 constexpr int KS = 64;                 // K elements per step
 constexpr int kRowBytes = KS * 2;      // one bf16 row of an X tile per step
 constexpr int kXChunks = kRowBytes / 16;
-constexpr int kWB = 64;                // packed bytes per weight row and block (4 ternary steps)
-constexpr int kWSpb = kWB / 16;        // steps per weight block
+constexpr int kWB = 64;                // packed bytes per weight row and block
 constexpr int kSGpb = 8;               // scale groups per scale block
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
 
-// Chunk c of weight row r within a block sits at position c ^ ((r >> 2) & 3): the 16 rows x 4
-// words one ds_read_b32 touches land in 64 different banks.
+// Chunk c of weight row r within a block sits at position c ^ ((r >> 2) & 3): the 16 rows one
+// 8-byte operand read touches land in 16 different 16-byte bank groups.
 __device__ __forceinline__ int w_pos(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg16 {
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
@@ -51,12 +58,16 @@ struct Cfg16 {
     static constexpr int S_SLOTS = BN * 2;
     static_assert(WM % 16 == 0 && WN % 16 == 0 && MB >= 1 && NB >= 1, "wave tile");
     static_assert(THREADS % kXChunks == 0, "a thread copies one chunk column of X");
+    static constexpr int W_STEP = KS * BITS / 8;             // packed bytes per row and step
+    static constexpr int W_SPB = kWB / W_STEP;               // steps per weight block
     static_assert(G == 64 || G == 128, "scale groups of 64 or 128");
+    static_assert(BITS == 1 || BITS == 2, "binary or ternary codes");
 };
 
-template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(ProblemGroup grp) {
-    using C = Cfg16<G, BM, BN, WAVES_M, WAVES_N>;
+    using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
+    constexpr int kWSpb = C::W_SPB;
     __shared__ __attribute__((aligned(16))) unsigned char xa0[C::X_TILE];
     __shared__ __attribute__((aligned(16))) unsigned char xa1[C::X_TILE];
     __shared__ __attribute__((aligned(16))) unsigned char wk0[C::W_BLOCK];
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
 
     const int kgroups = K / G;
     const int ksteps = K / KS;
-    const uint32_t w_row_bytes = uint32_t(K) / 4u;
+    const uint32_t w_row_bytes = uint32_t(K) * BITS / 8u;
     const uint32_t s_row_bytes = uint32_t(kgroups) * 2u;
 
     // ---- X: thread copies chunk position tid % 8 of rows tid / 8 + i * (THREADS / 8) ----
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
         }
     };
 
-    // ---- packed weights: block b = steps [4b, 4b+4) of the tile's BN rows, 64 bytes per row.
+    // ---- packed weights: block b = steps [b W_SPB, (b+1) W_SPB) of the tile's BN rows, 64 bytes per row.
     // Copy slot s = row s / 4, stored position s % 4 (holding source chunk w_pos(row, s % 4)).
     // Rows past N re-read row N-1.
     const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(N) * w_row_bytes);
@@ -143,21 +154,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
         }
     };
 
-    // Per-lane LDS offsets: weight row of each column block, its scale window.
+    // Per-lane LDS offsets: weight row of each column block (ternary: the lane's word pair of
+    // a step chunk; binary: the step's two words), its scale window.  The byte permute that
+    // gathers the lane's 16 codes from the two words: ternary halves (q & 1) of both words,
+    // binary bytes (q & 1) and (q & 1) + 2 of word q >> 1.
+    const uint32_t gather_sel =
+        BITS == 2 ? ((q & 1) ? 0x07060302u : 0x05040100u)
+                  : 0x0C0C0000u | (uint32_t(4 * (q >> 1) + (q & 1) + 2) << 8) | uint32_t(4 * (q >> 1) + (q & 1));
+    const uint32_t two_pair = opaque_two_pair();
     int w_rd[C::NB], s_rd[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
         const int r = wn0 + nb * 16 + l16;
         int n = n0 + r;
         n = n < N ? n : N - 1;
-        w_rd[nb] = r * kWB + 4 * q;
+        w_rd[nb] = r * kWB + (BITS == 2 ? 8 * (q >> 1) : 0);
         s_rd[nb] = r * 32 + int((uint32_t(n) * s_row_bytes) & 15u);
     }
 
     static_assert(C::WM % 16 == 0, "row blocks start at multiples of 16");
     int x_rd[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) x_rd[j] = x_off(wm0 + l16, 2 * q + j);
+    for (int j = 0; j < 2; ++j) x_rd[j] = x_off(wm0 + l16, 4 * (q >> 1) + (q & 1) + 2 * j);
 
     f32x4_t acc[C::MB][C::NB];
 #pragma unroll
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
     // A step's words and scales are read from LDS before any copy of the step is issued (the
     // compiler cannot tell which of the two buffers a step reads).
     struct Ops {
-        uint32_t w[C::NB];
+        u32x2_t w[C::NB];
         float sc[C::NB];
     };
     auto read_operands = [&](const unsigned char* wt, const unsigned char* st, int step, Ops& o) {
@@ -177,23 +195,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
             const int r = wn0 + nb * 16 + l16;
-            o.w[nb] = *reinterpret_cast<const uint32_t*>(wt + w_rd[nb] + (w_pos(r, wj) << 4));
-            // x 1/2: the operand holds 2c.  Also keeps the conversion out of the FMA (an fp16
-            // operand makes it v_fma_mix_f32, whose result does not share the accumulator's
-            // register and doubles the accumulator registers across the unrolled steps).
-            o.sc[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + grp_in_block * 2)) * 0.5f;
+            const int byte0 = wj * C::W_STEP;  // the step's bytes within the block row
+            o.w[nb] = *reinterpret_cast<const u32x2_t*>(wt + w_rd[nb] + (w_pos(r, byte0 >> 4) << 4) + (byte0 & 15));
+            // x 1/2 (ternary: the operand holds 2c) or x -1/2 (binary: -2c).  Also keeps the
+            // conversion out of the FMA (an fp16 operand makes it v_fma_mix_f32, whose result
+            // does not share the accumulator's register and doubles the accumulator registers
+            // across the unrolled steps).
+            o.sc[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + grp_in_block * 2)) *
+                       (BITS == 2 ? 0.5f : -0.5f);
         }
     };
 
     auto compute = [&](const unsigned char* xt, const Ops& o) {
+        // Codes of column block nb are expanded just before its first MFMA pair (row block 0),
+        // behind a scheduling fence: the expansion of block nb + 1 then runs while the matrix
+        // core works on block nb, instead of every wave of a SIMD expanding all its codes
+        // right after the step's barrier while the matrix core idles.
         u32x4_t bfr[C::NB][2];
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
+        auto expand = [&](int nb) {
             uint32_t d[8];
-            expand_ternary_word(o.w[nb], d);
+            const uint32_t codes = perm_b32(o.w[nb][1], o.w[nb][0], gather_sel);
+            if constexpr (BITS == 2)
+                expand_ternary_word(codes, d);
+            else
+                expand_binary_16(codes, two_pair, d);
             bfr[nb][0] = u32x4_t{d[0], d[1], d[2], d[3]};
             bfr[nb][1] = u32x4_t{d[4], d[5], d[6], d[7]};
-        }
+        };
         // Row blocks in order; within one, the MFMA pair of block (mb, nb) is issued before the
         // scale FMAs of the previous block, which use the other partial-sum registers.  The
         // activation operands of row block mb + 1 are read while row block mb computes.  Row
@@ -214,11 +242,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
                 const int b = mb * C::NB + nb;
+                if (mb == 0) expand(nb);
                 f32x4_t v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mb & 1][j], __builtin_bit_cast(bf16x8_t, bfr[nb][j]), v, 0,
                                                                 0, 0);
+                if (mb == 0) __builtin_amdgcn_sched_barrier(0);
                 tmp[b & 1] = v;
                 if (pb >= 0) {
                     const int pm = pb / C::NB, pn = pb % C::NB;
@@ -326,14 +356,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
             const uint32_t d0 = perm_b32(R, E, d0_sel), d1 = perm_b32(R, F, d1_sel);
             const int m = m0 + wm0 + mb * 16 + 4 * q + b4;
             if (m < M) {
-                typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
                 *reinterpret_cast<u32x2_t*>(p.Y + int64_t(m) * N + nblk + (l16 & ~3)) = u32x2_t{d0, d1};
             }
         }
     }
 }
 
-template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
     ProblemGroup grp{};
     int total = 0;
@@ -343,19 +372,22 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
         grp.tile_end[i] = total;
     }
     grp.count = count;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BM, BN, WAVES_M, WAVES_N>), dim3(total), dim3(64 * WAVES_M * WAVES_N),
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N>), dim3(total), dim3(64 * WAVES_M * WAVES_N),
                        0, stream, grp);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool tile16_supported(int g, int bits) { return bits == 2 && (g == 64 || g == 128); }
+bool tile16_supported(int g, int bits) { return (bits == 1 || bits == 2) && (g == 64 || g == 128); }
 
-hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, hipStream_t stream) {
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
     // 288 x 192 in 12 waves of 96 x 48: LDS 72 KB (X) + 24 KB (W) + 12 KB (S)
-    return g == 64 ? launch_cfg16<64, 288, 192, 3, 4>(probs, count, stream)
-                   : launch_cfg16<128, 288, 192, 3, 4>(probs, count, stream);
+    if (bits == 2)
+        return g == 64 ? launch_cfg16<64, 2, 288, 192, 3, 4>(probs, count, stream)
+                       : launch_cfg16<128, 2, 288, 192, 3, 4>(probs, count, stream);
+    return g == 64 ? launch_cfg16<64, 1, 288, 192, 3, 4>(probs, count, stream)
+                   : launch_cfg16<128, 1, 288, 192, 3, 4>(probs, count, stream);
 }
 
 }  // namespace lowbit

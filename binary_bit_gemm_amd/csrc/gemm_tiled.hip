@@ -365,14 +365,18 @@ namespace {
 
 struct TileShape {
     int variant, bm, bn, per_cu;  // workgroups resident per compute unit
-    float eff;                    // relative per-FLOP efficiency of the tile (measured order)
+    float eff, eff_binary;        // relative per-FLOP efficiency of the tile, ternary / binary
 };
 
+// Measured at M = 4608 on the denoise-step shapes: a 288 x 192 tile does ~0.87 (ternary) and
+// ~0.82 (binary) of a 256 x 256 tile's work per unit time (smaller wave tiles: less operand
+// reuse), which about cancels (ternary) or outweighs (binary) the 16% of units a 256 x 256
+// grid leaves idle at N = 3072.
 constexpr TileShape kTiles[] = {
-    {TILE_256x256, 256, 256, 1, 1.00f},
-    {TILE_288x192, 288, 192, 1, 1.00f},
-    {TILE_128x256, 128, 256, 2, 0.92f},
-    {TILE_64x256, 64, 256, 2, 0.75f},
+    {TILE_256x256, 256, 256, 1, 1.00f, 1.00f},
+    {TILE_288x192, 288, 192, 1, 0.87f, 0.82f},
+    {TILE_128x256, 128, 256, 2, 0.92f, 0.92f},
+    {TILE_64x256, 64, 256, 2, 0.75f, 0.75f},
 };
 
 }  // namespace
@@ -387,7 +391,7 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
             tiles += int64_t((probs[i].M + t.bm - 1) / t.bm) * ((probs[i].N + t.bn - 1) / t.bn);
         const int64_t slots = int64_t(kComputeUnits) * t.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
-        const double cost = double(rounds) * t.per_cu * t.bm * t.bn / t.eff;
+        const double cost = double(rounds) * t.per_cu * t.bm * t.bn / (bits == 1 ? t.eff_binary : t.eff);
         if (best_cost == 0.0 || cost < best_cost) {
             best = t.variant;
             best_cost = cost;
@@ -414,7 +418,7 @@ const char* tile_variant_name(int variant) {
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream) {
     if (variant == TILE_288x192) {
-        if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, stream);
+        if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, bits, stream);
         variant = TILE_256x256;
     }
     if (bits == 2) {

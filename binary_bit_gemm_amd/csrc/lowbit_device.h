@@ -16,6 +16,7 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 // v_perm_b32: byte i of the result is byte sel.byte[i] of the 8-byte value {hi:lo}
 // (0..3 -> lo, 4..7 -> hi); selector 0x0C yields 0x00.
@@ -63,6 +64,26 @@ __device__ __forceinline__ void expand_binary_word(uint32_t w, uint32_t out[NOUT
         const int b = d >> 2, j = 2 * (d & 3);
         out[d] = perm_b32(e[j + 1], e[j], pair_sel(b));
     }
+}
+
+// 0x40004000 (a pair of bf16 2.0) in a register whose value the compiler does not see, so that
+// (x << s | it) & mask stays two instructions (v_lshl_or_b32 + v_and_b32) instead of being
+// rewritten as a shift, an and and an or (a three-operand instruction takes no literal here).
+__device__ __forceinline__ uint32_t opaque_two_pair() {
+    uint32_t c;
+    asm("s_mov_b32 %0, 0x40004000" : "=s"(c));
+    return c;
+}
+
+// Sixteen binary codes, the low 16 bits of h (the high bits zero), to 8 operand dwords,
+// out[d] = bf16 pair (-2*c[2d], -2*c[2d+1]), in 17 instructions:
+//   v = h | h << 15, so bit 2d of v is code 2d and bit 16 + 2d is code 2d + 1;
+//   out[d] = ((v << (15 - 2d)) | 0x40004000) & 0xC000C000 puts them on the two sign bits.
+// `two_pair` is opaque_two_pair().
+__device__ __forceinline__ void expand_binary_16(uint32_t h, uint32_t two_pair, uint32_t out[8]) {
+    const uint32_t v = h | (h << 15);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) out[d] = ((v << (15 - 2 * d)) | two_pair) & 0xC000C000u;
 }
 
 // LDS tiles are stored as rows of 128-byte (or 256-byte) lines of 16-byte chunks; chunk c of

@@ -75,7 +75,7 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits);
 int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
 const char* tile_variant_name(int variant);
 bool tile16_supported(int g, int bits);
-hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, hipStream_t stream);
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit

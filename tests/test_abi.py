@@ -102,9 +102,12 @@ def test_variant_choice():
     assert lb.variant(4608, 3072, 3072, 64, 2) == "tile288x192"
     assert lb.variant(4608, 18432, 3072, 64, 2) == "tile288x192"
     assert lb.variant(4608, 3072, 12288, 128, 2) == "tile288x192"
-    # the 16x16-block kernel is ternary g = 64 / 128 only
+    # the 16x16-block kernel takes g = 64 / 128; for binary codes it does less work per unit
+    # time than 256 x 256 by more than the idle units cost, so binary stays on 256 x 256
     assert lb.variant(4608, 3072, 3072, 64, 1) == "tile256x256"
+    assert lb.variant(4608, 3072, 12288, 128, 1) == "tile256x256"
     assert lb.variant(4608, 3072, 3072, 32, 2) == "tile256x256"
+    assert lb.variant(4608, 3072, 3072, 32, 1) == "tile256x256"
     assert lb.variant(64, 256, 256, 64, 2).startswith("tile")
 
 

@@ -113,6 +113,20 @@ def test_every_variant(variant, M, monkeypatch):
             _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{variant} M={M} g{g} b{bits}")
 
 
+@pytest.mark.parametrize("bits", [2, 1])
+@pytest.mark.parametrize("M,N,K,g", [(600, 400, 1280, 64), (300, 592, 3072, 128), (289, 208, 64, 64),
+                                     (577, 192, 8448, 128)])
+def test_tile288_several_blocks(M, N, K, g, bits, monkeypatch):
+    # the 16x16-block kernel over several weight blocks (64 bytes of a row: 4 ternary or 8
+    # binary steps) and scale blocks, a last weight block that runs past the row (K % 512 !=
+    # 0 for binary), a single step, and ragged tiles in both directions
+    monkeypatch.setenv("LOWBIT_VARIANT", "tile288")
+    assert lb.variant(M, N, K, g, bits) == "tile288x192"
+    inp = _inputs(M, N, K, g, bits, seed=11)
+    y, _ = run_gemm(inp, g, bits)
+    _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"tile288 {M}x{N}x{K} g{g} b{bits}")
+
+
 def test_empty_and_k0():
     t = torch()
     x = t.zeros((0, 64), dtype=t.bfloat16, device="cuda")
@@ -218,7 +232,7 @@ def _sample_rows(M, seed):
     return np.array(sorted(rows))
 
 
-FULL = W.RES512_TERNARY + W.RES512_BINARY + W.RES1024_TERNARY
+FULL = W.RES512_TERNARY + W.RES512_BINARY + W.RES1024_TERNARY + W.RES1024_BINARY_G128
 
 
 @pytest.mark.parametrize("prob", FULL, ids=lambda p: p.name)

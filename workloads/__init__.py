@@ -128,6 +128,10 @@ RES512_BINARY = [Problem(f"m1536_{n}_bin", 1536, N, K, BINARY, 64, 2, i)
                  for i, (n, N, K) in enumerate(_BLOCK_SHAPES)]
 RES1024_TERNARY = [Problem(f"m4608_{n}", 4608, N, K, TERNARY, 64, 3, i)
                    for i, (n, N, K) in enumerate(_BLOCK_SHAPES + [("single_out", 3072, 12288)])]
+# the binary model card's own format: 1-bit codes with one fp16 scale per 128 weights
+# ("bonsai-image-binary-4B-gemlite-1bit" model card, "Binary Weight Representation: 1-bit g128")
+RES1024_BINARY_G128 = [Problem(f"m4608_{n}_bin128", 4608, N, K, BINARY, 128, 5, i)
+                       for i, (n, N, K) in enumerate(_BLOCK_SHAPES + [("single_out", 3072, 12288)])]
 
 
 def denoise_step_sweep(M_img: int = 4096, M_txt: int = 512, bits: int = TERNARY, g: int = 64,
@@ -178,6 +182,7 @@ CONFIGS = {
     "res512_ternary": RES512_TERNARY,
     "res512_binary": RES512_BINARY,
     "res1024_ternary": RES1024_TERNARY,
+    "res1024_binary_g128": RES1024_BINARY_G128,
 }
 
 
