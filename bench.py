@@ -35,7 +35,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 # summary of a workload is used only while the sources of the kernels it runs are unchanged.
 VARIANT_SOURCES = {
     "tile256x256": ["gemm_tiled.hip"], "tile256x128": ["gemm_tiled.hip"], "tile128x256": ["gemm_tiled.hip"],
-    "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "skinny": ["gemm_skinny.hip"],
+    "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "tile96x192": ["gemm_tile16.hip"],
+    "skinny": ["gemm_skinny.hip"],
     "resident": ["gemm_resident.hip"],
 }
 COMMON_SOURCES = ["lowbit_device.h", "lowbit_internal.h", "gemm_grouped.hip"]

@@ -25,6 +25,7 @@ int forced_tile() {
     if (std::strcmp(v, "tile128") == 0) return TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return TILE_64x256;
     if (std::strcmp(v, "tile288") == 0) return TILE_288x192;
+    if (std::strcmp(v, "tile96") == 0) return TILE_96x192;
     return -1;
 }
 

@@ -381,13 +381,21 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
 
 bool tile16_supported(int g, int bits) { return (bits == 1 || bits == 2) && (g == 64 || g == 128); }
 
-hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
-    // 288 x 192 in 12 waves of 96 x 48: LDS 72 KB (X) + 24 KB (W) + 12 KB (S)
+template <int G, int BITS>
+hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hipStream_t stream) {
+    // 288 x 192 in 12 waves of 96 x 48: LDS 72 KB (X) + 24 KB (W) + 12 KB (S).
+    // 96 x 192 in 4 waves of 96 x 48 (LDS 60 KB): 1536 x 3072 outputs are exactly 256 tiles.
+    if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
+    return launch_cfg16<G, BITS, 288, 192, 3, 4>(probs, count, stream);
+}
+
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,
+                                    hipStream_t stream) {
     if (bits == 2)
-        return g == 64 ? launch_cfg16<64, 2, 288, 192, 3, 4>(probs, count, stream)
-                       : launch_cfg16<128, 2, 288, 192, 3, 4>(probs, count, stream);
-    return g == 64 ? launch_cfg16<64, 1, 288, 192, 3, 4>(probs, count, stream)
-                   : launch_cfg16<128, 1, 288, 192, 3, 4>(probs, count, stream);
+        return g == 64 ? launch_variant16<64, 2>(probs, count, variant, stream)
+                       : launch_variant16<128, 2>(probs, count, variant, stream);
+    return g == 64 ? launch_variant16<64, 1>(probs, count, variant, stream)
+                   : launch_variant16<128, 1>(probs, count, variant, stream);
 }
 
 }  // namespace lowbit

@@ -371,12 +371,14 @@ struct TileShape {
 // Measured at M = 4608 on the denoise-step shapes: a 288 x 192 tile does ~0.87 (ternary) and
 // ~0.82 (binary) of a 256 x 256 tile's work per unit time (smaller wave tiles: less operand
 // reuse), which about cancels (ternary) or outweighs (binary) the 16% of units a 256 x 256
-// grid leaves idle at N = 3072.
+// grid leaves idle at N = 3072.  A 96 x 192 tile (four waves, one per SIMD) does ~0.54; it
+// pays where nothing larger fills the chip (1536 x 3072: 256 tiles).
 constexpr TileShape kTiles[] = {
     {TILE_256x256, 256, 256, 1, 1.00f, 1.00f},
     {TILE_288x192, 288, 192, 1, 0.87f, 0.82f},
     {TILE_128x256, 128, 256, 2, 0.92f, 0.92f},
     {TILE_64x256, 64, 256, 2, 0.75f, 0.75f},
+    {TILE_96x192, 96, 192, 1, 0.54f, 0.51f},
 };
 
 }  // namespace
@@ -385,7 +387,12 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
     int best = TILE_64x256;
     double best_cost = 0.0;
     for (const TileShape& t : kTiles) {
-        if (t.variant == TILE_288x192 && !tile16_supported(g, bits)) continue;
+        if (is_tile16_variant(t.variant) && !tile16_supported(g, bits)) continue;
+        if (t.variant == TILE_96x192) {  // measured at M = 1536; below M = 1024 it stays unused
+            bool small = false;
+            for (int i = 0; i < count; ++i) small = small || probs[i].M < 1024;
+            if (small) continue;
+        }
         int64_t tiles = 0;
         for (int i = 0; i < count; ++i)
             tiles += int64_t((probs[i].M + t.bm - 1) / t.bm) * ((probs[i].N + t.bn - 1) / t.bn);
@@ -411,14 +418,15 @@ const char* tile_variant_name(int variant) {
         case TILE_256x256: return "tile256x256";
         case TILE_128x256: return "tile128x256";
         case TILE_288x192: return "tile288x192";
+        case TILE_96x192: return "tile96x192";
         default: return "tile64x256";
     }
 }
 
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream) {
-    if (variant == TILE_288x192) {
-        if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, bits, stream);
+    if (is_tile16_variant(variant)) {
+        if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, bits, variant, stream);
         variant = TILE_256x256;
     }
     if (bits == 2) {

@@ -56,7 +56,8 @@ int device_check() {
 }
 
 // Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | resident | tile256 | tile256w |
-// tile128 | tile64 | tile288 (the last falls back to tile256w where the 16x16 kernel does not apply)
+// tile128 | tile64 | tile288 | tile96 (the last two fall back to tile256w where the 16x16 kernel does not
+// apply)
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
@@ -66,6 +67,7 @@ int forced_variant() {
     if (std::strcmp(v, "tile128") == 0) return lowbit::TILE_128x256;
     if (std::strcmp(v, "tile64") == 0) return lowbit::TILE_64x256;
     if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
+    if (std::strcmp(v, "tile96") == 0) return lowbit::TILE_96x192;
     if (std::strcmp(v, "resident") == 0) return 102;
     return -1;
 }
@@ -218,7 +220,7 @@ const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits
     int v = choose_variant(M, N, K, g, bits);
     if (v == 100) return "skinny";
     if (v == 102) return "resident";
-    if (v == lowbit::TILE_288x192 && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
+    if (lowbit::is_tile16_variant(v) && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
     return lowbit::tile_variant_name(v);
 }
 

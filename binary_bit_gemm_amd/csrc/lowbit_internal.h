@@ -32,8 +32,11 @@ hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K,
                          hipStream_t stream);
 
 // Tiled MFMA kernels (LDS-staged X, packed weights and scales).  `variant` selects the tile;
-// TILE_288x192 is the 16x16x32-block kernel (ternary, g = 64 or 128 only).
-enum TileVariant { TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4 };
+// TILE_288x192 and TILE_96x192 are the 16x16x32-block kernel (g = 64 or 128 only).
+enum TileVariant {
+    TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5
+};
+inline bool is_tile16_variant(int v) { return v == TILE_288x192 || v == TILE_96x192; }
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
@@ -75,7 +78,8 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits);
 int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
 const char* tile_variant_name(int variant);
 bool tile16_supported(int g, int bits);
-hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
+hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,
+                                    hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit
