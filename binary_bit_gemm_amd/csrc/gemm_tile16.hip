@@ -6,7 +6,8 @@
 // tiles of 256 x 256 on 256 compute units -- 16% of the chip idles.  16x16 blocks allow a
 // 288 x 192 tile (12 waves of 96 x 48): 4608 x 3072 is then exactly 256 tiles, 4608 x 9216
 // and 4608 x 18432 whole multiples of 256.  Per FLOP the 16x16x32 instruction needs the same
-// operand bytes, the same code expansion and the same scale FMAs as the 32x32x16 one.
+// operand bytes, the same code expansion and the same scale FMAs as the 32x32x16 one.  The
+// same kernel with 4 waves makes a 96 x 192 tile: 1536 x 3072 is then exactly 256 tiles.
 //
 // Data movement is that of the 32x32 kernel (direct-to-LDS copies of X per 64-element step,
 // of packed weights in 64-byte row blocks, of scales in 8-group blocks; everything
