@@ -18,11 +18,13 @@
 // (v_permlane32_swap, v_permlane16_swap) transpose the 4x4 (lane quarter, word) blocks so
 // that register c holds, in lane quarter q, word q of chunk c.  Then each MFMA takes eight
 // consecutive codes of every quarter's word of one chunk, so its 32 K positions lie in one
-// chunk -- and a chunk lies in one scale group for the supported (bits, g): ternary g = 64
-// or 128, binary g = 128.  The group scale multiplies the chunk's exact partial sum after
-// the MFMA, in fp32 (w = scale_g * b, model card "Binary Weight Representation: 1-bit
-// g128"); the operand holds 2c (ternary) or -2c (binary) and the factor +-1/2 is applied
-// once to the final sum.
+// chunk -- and a chunk lies in one scale group for ternary g = 64 or 128 and binary g = 128.
+// A binary chunk with g = 64 spans two groups, quarters 0-1 the first and 2-3 the second:
+// each of its MFMAs runs twice, with the activation operand of the other group's quarters
+// set to zero, and each result takes its own group's scale.  The group scale multiplies
+// the exact partial sum after the MFMA, in fp32 (w = scale_g * b, model card "Binary
+// Weight Representation: 1-bit g128"); the operand holds 2c (ternary) or -2c (binary) and
+// the factor +-1/2 is applied once to the final sum.
 #include <cstdlib>
 
 #include "lowbit_device.h"
@@ -44,10 +46,11 @@ struct SkinnyFmt {
 template <int BITS, int G, int MB, int NCB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup grp) {
     using F = SkinnyFmt<BITS>;
-    constexpr int GPS = F::STEP / G;     // scale groups per step
-    constexpr int CPG = G / F::CHUNK;    // chunks per scale group (1 or 2)
-    static_assert(G % F::CHUNK == 0, "a chunk must lie in one scale group");
-    static_assert(GPS == 2 || GPS == 4, "scale groups per step");
+    constexpr int GPS = F::STEP / G;                      // scale groups per step
+    constexpr bool kSplitChunk = F::CHUNK > G;            // binary g = 64: two groups per chunk
+    constexpr int CPG = kSplitChunk ? 1 : G / F::CHUNK;   // chunks per scale group (1 or 2)
+    static_assert(G % F::CHUNK == 0 || F::CHUNK == 2 * G, "a chunk lies in one or two scale groups");
+    static_assert(GPS == 2 || GPS == 4 || GPS == 8, "scale groups per step");
 
     // Activations of one step for the ternary single-row-block case go through LDS: each
     // wave copies its own 16 x 256 slice with contiguous 16-byte direct-to-LDS loads (two
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
     struct Stage {
         u32x4_t w[NCB];
         bf16x8_t x[MB][F::XPS];
-        u32x2_t s[NCB];
+        u32x4_t s[NCB];
     };
 
     // Loads of a step past the wave's range go through empty resources: they are issued (so
@@ -158,10 +161,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
         const __amdgpu_buffer_rsrc_t sr = make_rsrc(s_wg + sk, live ? s_bytes - sk : 0u);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            if constexpr (GPS == 4) {
-                st.s[cb] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, s_off[cb], 0, 0));
+            if constexpr (GPS == 8) {
+                st.s[cb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off[cb], 0, 0));
+            } else if constexpr (GPS == 4) {
+                const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, s_off[cb], 0, 0));
+                st.s[cb] = u32x4_t{v[0], v[1], 0u, 0u};
             } else {
-                st.s[cb] = u32x2_t{__builtin_amdgcn_raw_buffer_load_b32(sr, s_off[cb], 0, 0), 0u};
+                st.s[cb] = u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(sr, s_off[cb], 0, 0), 0u, 0u, 0u};
             }
         }
         // Keep the scheduler from sinking these loads towards their use (it would trade the
@@ -175,9 +181,59 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    auto scale_of = [&](const u32x4_t& sv, int gi) {  // fp16 scale of group gi of the step
+        const uint32_t sw = sv[gi >> 1];
+        return half_bits_to_float(uint16_t((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+    };
+    const bool first_half = q < 2;  // binary g = 64: the lane's codes lie in the chunk's first group
+
     auto compute = [&](Stage& st, const unsigned char* xbuf) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) transpose_words(st.w[cb]);
+        if constexpr (kSplitChunk) {
+            static_assert(!kXLds, "split chunks take their activations from registers");
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // the chunk's activation operands, once with the second group's quarters zeroed
+                // and once with the first group's
+                bf16x8_t xg[2][MB][F::MPC];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < F::MPC; ++j) {
+                        const u32x4_t v = __builtin_bit_cast(u32x4_t, st.x[mb][c * F::MPC + j]);
+                        u32x4_t lo, hi;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            lo[e] = first_half ? v[e] : 0u;
+                            hi[e] = first_half ? 0u : v[e];
+                        }
+                        xg[0][mb][j] = __builtin_bit_cast(bf16x8_t, lo);
+                        xg[1][mb][j] = __builtin_bit_cast(bf16x8_t, hi);
+                    }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    uint32_t d[F::CPW / 2];
+                    expand_binary_word<16>(st.w[cb][c], d);
+                    const float s0 = scale_of(st.s[cb], 2 * c), s1 = scale_of(st.s[cb], 2 * c + 1);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = 0; j < F::MPC; ++j) {
+                            const bf16x8_t b =
+                                __builtin_bit_cast(bf16x8_t, u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
+                            t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[0][mb][j], b, t0, 0, 0, 0);
+                            t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[1][mb][j], b, t1, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[mb][cb][i] = __builtin_fmaf(s1, t1[i], __builtin_fmaf(s0, t0[i], acc[mb][cb][i]));
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -188,9 +244,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
                 } else {
                     expand_binary_word<16>(st.w[cb][c], d);
                 }
-                const int gi = c / CPG;  // group within the step
-                const uint32_t sw = st.s[cb][gi >> 1];
-                const float sc = half_bits_to_float(uint16_t((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                const float sc = scale_of(st.s[cb], c / CPG);  // group within the step
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     f32x4_t t = {0.f, 0.f, 0.f, 0.f};
@@ -314,7 +368,7 @@ int pick_ncb(const GemmProblem* probs, int count) {
 
 }  // namespace
 
-bool skinny_supported(int g, int bits) { return bits == 2 ? (g == 64 || g == 128) : g == 128; }
+bool skinny_supported(int g, int bits) { return g == 64 || g == 128; }
 
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits) {
     (void)N;
@@ -330,7 +384,8 @@ hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, 
         return g == 64 ? launch_bits_g<2, 64>(probs, count, max_m, ncb, stream)
                        : launch_bits_g<2, 128>(probs, count, max_m, ncb, stream);
     }
-    return launch_bits_g<1, 128>(probs, count, max_m, ncb, stream);
+    return g == 64 ? launch_bits_g<1, 64>(probs, count, max_m, ncb, stream)
+                   : launch_bits_g<1, 128>(probs, count, max_m, ncb, stream);
 }
 
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream) {

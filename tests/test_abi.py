@@ -117,8 +117,9 @@ def test_variant_choice():
 
 
 def test_skinny_variant_choice():
-    """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) when a 16-byte chunk of
-    a packed row lies in one scale group and K is a whole number of 64-byte row steps."""
+    """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) for g = 64 / 128 when K
+    is a whole number of 64-byte row steps (a binary chunk of 128 codes spans two groups of
+    64; the kernel runs each of its MFMAs once per group)."""
     assert lb.variant(16, 3072, 3072, 64, 2) == "skinny"
     assert lb.variant(1, 3072, 3072, 128, 2) == "skinny"
     assert lb.variant(32, 3072, 12288, 64, 2) == "skinny"
@@ -126,7 +127,8 @@ def test_skinny_variant_choice():
     assert lb.variant(16, 3072, 3072, 32, 2) == "tile64x256"     # group of 32 < chunk of 64
     assert lb.variant(16, 3072, 320, 64, 2) == "tile64x256"      # K % 256 != 0
     assert lb.variant(16, 3072, 3072, 128, 1) == "skinny"
-    assert lb.variant(16, 3072, 3072, 64, 1) == "tile64x256"     # binary chunk is 128 codes
+    assert lb.variant(16, 3072, 3072, 64, 1) == "skinny"         # binary chunk over two groups
+    assert lb.variant(16, 3072, 3072, 32, 1) == "tile64x256"     # group of 32
     assert lb.variant(16, 3072, 2816, 128, 1) == "tile64x256"    # K % 512 != 0
     assert lb.variant(17, 3072, 3072, 128, 1) == "tile64x256"
 

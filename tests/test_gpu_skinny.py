@@ -45,7 +45,7 @@ def _is_zero(bits):
 
 
 # (bits, g, K): K = 5 row steps, so the four waves get 1, 1, 1 and 2 steps
-_FORMATS = [(2, 64, 1280), (2, 128, 1280), (1, 128, 2560)]
+_FORMATS = [(2, 64, 1280), (2, 128, 1280), (1, 128, 2560), (1, 64, 2560)]
 
 
 @pytest.mark.parametrize("bits,g,K", _FORMATS)
@@ -63,8 +63,9 @@ def test_rows(M, g):
 
 
 @pytest.mark.parametrize("M", [1, 9, 16])
-def test_rows_binary(M):
-    _check(M, 1040, 1536, 128, 1, seed=2, what="rows binary")
+@pytest.mark.parametrize("g", [64, 128])
+def test_rows_binary(M, g):
+    _check(M, 1040, 1536, g, 1, seed=2, what=f"rows binary g{g}")
 
 
 @pytest.mark.parametrize("K", [256, 512, 768, 2048, 9216])
@@ -73,7 +74,7 @@ def test_step_counts(K):
     _check(16, 512, K, 64, 2, seed=3, what="steps")
 
 
-@pytest.mark.parametrize("bits,g", [(2, 64), (2, 128), (1, 128)])
+@pytest.mark.parametrize("bits,g", [(2, 64), (2, 128), (1, 128), (1, 64)])
 def test_one_hot_bit_exact(bits, g):
     M, N, K = 16, 64, 1024
     x = W.gen_x(W.rng_for(4, 41, 0), M, K)
@@ -120,7 +121,7 @@ def test_zero_codes_scales_and_unused_field():
     assert not y.float().abs().sum().item()
 
 
-@pytest.mark.parametrize("bits,g", [(2, 64), (1, 128)])
+@pytest.mark.parametrize("bits,g", [(2, 64), (1, 128), (1, 64)])
 def test_linearity_bit_exact(bits, g):
     M, N, K = 16, 512, 2048
     inp = _inputs(M, N, K, g, bits, seed=6)
