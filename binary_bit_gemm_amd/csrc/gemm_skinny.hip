@@ -19,9 +19,10 @@
 // that register c holds, in lane quarter q, word q of chunk c.  Then each MFMA takes eight
 // consecutive codes of every quarter's word of one chunk, so its 32 K positions lie in one
 // chunk -- and a chunk lies in one scale group for ternary g = 64 or 128 and binary g = 128.
-// A binary chunk with g = 64 spans two groups, quarters 0-1 the first and 2-3 the second:
-// each of its MFMAs runs twice, with the activation operand of the other group's quarters
-// set to zero, and each result takes its own group's scale.  The group scale multiplies
+// A smaller group splits the chunk by lane quarters (ternary g = 32 and binary g = 64: two
+// groups, quarters 0-1 and 2-3; binary g = 32: four, one per quarter): each MFMA of the
+// chunk then runs once per group, with the activation operand of the other groups'
+// quarters set to zero, and each result takes its own group's scale.  The group scale multiplies
 // the exact partial sum after the MFMA, in fp32 (w = scale_g * b, model card "Binary
 // Weight Representation: 1-bit g128"); the operand holds 2c (ternary) or -2c (binary) and
 // the factor +-1/2 is applied once to the final sum.
@@ -47,10 +48,12 @@ template <int BITS, int G, int MB, int NCB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup grp) {
     using F = SkinnyFmt<BITS>;
     constexpr int GPS = F::STEP / G;                      // scale groups per step
-    constexpr bool kSplitChunk = F::CHUNK > G;            // binary g = 64: two groups per chunk
+    constexpr bool kSplitChunk = F::CHUNK > G;            // groups smaller than a chunk
+    constexpr int GPC = kSplitChunk ? F::CHUNK / G : 1;   // scale groups per chunk (1, 2 or 4)
     constexpr int CPG = kSplitChunk ? 1 : G / F::CHUNK;   // chunks per scale group (1 or 2)
-    static_assert(G % F::CHUNK == 0 || F::CHUNK == 2 * G, "a chunk lies in one or two scale groups");
-    static_assert(GPS == 2 || GPS == 4 || GPS == 8, "scale groups per step");
+    constexpr int SD = GPS / 2;                           // scale dwords per row and step
+    static_assert(G % F::CHUNK == 0 || GPC == 2 || GPC == 4, "a chunk lies in 1, 2 or 4 scale groups");
+    static_assert(GPS == 2 || GPS == 4 || GPS == 8 || GPS == 16, "scale groups per step");
 
     // Activations of one step for the ternary single-row-block case go through LDS: each
     // wave copies its own 16 x 256 slice with contiguous 16-byte direct-to-LDS loads (two
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
     struct Stage {
         u32x4_t w[NCB];
         bf16x8_t x[MB][F::XPS];
-        u32x4_t s[NCB];
+        uint32_t s[NCB][SD];
     };
 
     // Loads of a step past the wave's range go through empty resources: they are issued (so
@@ -161,13 +164,20 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
         const __amdgpu_buffer_rsrc_t sr = make_rsrc(s_wg + sk, live ? s_bytes - sk : 0u);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            if constexpr (GPS == 8) {
-                st.s[cb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off[cb], 0, 0));
-            } else if constexpr (GPS == 4) {
+            if constexpr (SD >= 4) {
+#pragma unroll
+                for (int h = 0; h < SD / 4; ++h) {
+                    const u32x4_t v = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off[cb] + uint32_t(16 * h), 0, 0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st.s[cb][4 * h + e] = v[e];
+                }
+            } else if constexpr (SD == 2) {
                 const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, s_off[cb], 0, 0));
-                st.s[cb] = u32x4_t{v[0], v[1], 0u, 0u};
+                st.s[cb][0] = v[0];
+                st.s[cb][1] = v[1];
             } else {
-                st.s[cb] = u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(sr, s_off[cb], 0, 0), 0u, 0u, 0u};
+                st.s[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off[cb], 0, 0);
             }
         }
         // Keep the scheduler from sinking these loads towards their use (it would trade the
@@ -181,54 +191,58 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_skinny_kernel(ProblemGroup
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto scale_of = [&](const u32x4_t& sv, int gi) {  // fp16 scale of group gi of the step
+    auto scale_of = [&](const uint32_t (&sv)[SD], int gi) {  // fp16 scale of group gi of the step
         const uint32_t sw = sv[gi >> 1];
         return half_bits_to_float(uint16_t((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
     };
-    const bool first_half = q < 2;  // binary g = 64: the lane's codes lie in the chunk's first group
+    const int lane_group = q / (4 / GPC);  // split chunks: the chunk group of the lane's codes
 
     auto compute = [&](Stage& st, const unsigned char* xbuf) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) transpose_words(st.w[cb]);
         if constexpr (kSplitChunk) {
-            static_assert(!kXLds, "split chunks take their activations from registers");
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                // the chunk's activation operands, once with the second group's quarters zeroed
-                // and once with the first group's
-                bf16x8_t xg[2][MB][F::MPC];
+                // the chunk's activation operands, one copy per group with the other groups'
+                // quarters zeroed (a lane-constant select)
+                bf16x8_t xg[GPC][MB][F::MPC];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int j = 0; j < F::MPC; ++j) {
-                        const u32x4_t v = __builtin_bit_cast(u32x4_t, st.x[mb][c * F::MPC + j]);
-                        u32x4_t lo, hi;
+                        const u32x4_t v = __builtin_bit_cast(
+                            u32x4_t, kXLds ? *reinterpret_cast<const bf16x8_t*>(xbuf + x_rd[c * F::MPC + j])
+                                           : st.x[mb][c * F::MPC + j]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            lo[e] = first_half ? v[e] : 0u;
-                            hi[e] = first_half ? 0u : v[e];
+                        for (int h = 0; h < GPC; ++h) {
+                            u32x4_t m;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) m[e] = lane_group == h ? v[e] : 0u;
+                            xg[h][mb][j] = __builtin_bit_cast(bf16x8_t, m);
                         }
-                        xg[0][mb][j] = __builtin_bit_cast(bf16x8_t, lo);
-                        xg[1][mb][j] = __builtin_bit_cast(bf16x8_t, hi);
                     }
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     uint32_t d[F::CPW / 2];
-                    expand_binary_word<16>(st.w[cb][c], d);
-                    const float s0 = scale_of(st.s[cb], 2 * c), s1 = scale_of(st.s[cb], 2 * c + 1);
+                    if constexpr (BITS == 2)
+                        expand_ternary_word(st.w[cb][c], d);
+                    else
+                        expand_binary_word<16>(st.w[cb][c], d);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        f32x4_t t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int j = 0; j < F::MPC; ++j) {
-                            const bf16x8_t b =
-                                __builtin_bit_cast(bf16x8_t, u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
-                            t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[0][mb][j], b, t0, 0, 0, 0);
-                            t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg[1][mb][j], b, t1, 0, 0, 0);
+                        for (int h = 0; h < GPC; ++h) {
+                            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int j = 0; j < F::MPC; ++j)
+                                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    xg[h][mb][j],
+                                    __builtin_bit_cast(bf16x8_t, u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]}),
+                                    t, 0, 0, 0);
+                            const float sc = scale_of(st.s[cb], GPC * c + h);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[mb][cb][i] = __builtin_fmaf(sc, t[i], acc[mb][cb][i]);
                         }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mb][cb][i] = __builtin_fmaf(s1, t1[i], __builtin_fmaf(s0, t0[i], acc[mb][cb][i]));
                     }
                 }
             }
@@ -319,13 +333,13 @@ hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
 
 // Wider stripes only where the registers allow them: four column blocks for one row block of
 // ternary codes, two for binary codes (twice the activation operands per step), one for two
-// row blocks.
+// row blocks and for binary codes with groups of 32 (four masked operand copies per chunk).
 template <int BITS, int G, int MB>
 hipError_t launch_mb(const GemmProblem* probs, int count, int ncb, hipStream_t stream) {
     if constexpr (MB == 1 && BITS == 2) {
         if (ncb >= 4) return launch_cfg<BITS, G, MB, 4>(probs, count, stream);
     }
-    if constexpr (MB == 1) {
+    if constexpr (MB == 1 && !(BITS == 1 && G == 32)) {
         if (ncb >= 2) return launch_cfg<BITS, G, MB, 2>(probs, count, stream);
     }
     return launch_cfg<BITS, G, MB, 1>(probs, count, stream);
@@ -368,7 +382,10 @@ int pick_ncb(const GemmProblem* probs, int count) {
 
 }  // namespace
 
-bool skinny_supported(int g, int bits) { return g == 64 || g == 128; }
+bool skinny_supported(int g, int bits) {
+    (void)bits;
+    return g == 32 || g == 64 || g == 128;
+}
 
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits) {
     (void)N;
@@ -381,11 +398,17 @@ hipError_t launch_gemm_skinny_group(const GemmProblem* probs, int count, int g, 
     for (int i = 0; i < count; ++i) max_m = probs[i].M > max_m ? probs[i].M : max_m;
     const int ncb = pick_ncb(probs, count);
     if (bits == 2) {
-        return g == 64 ? launch_bits_g<2, 64>(probs, count, max_m, ncb, stream)
-                       : launch_bits_g<2, 128>(probs, count, max_m, ncb, stream);
+        switch (g) {
+            case 32: return launch_bits_g<2, 32>(probs, count, max_m, ncb, stream);
+            case 64: return launch_bits_g<2, 64>(probs, count, max_m, ncb, stream);
+            default: return launch_bits_g<2, 128>(probs, count, max_m, ncb, stream);
+        }
     }
-    return g == 64 ? launch_bits_g<1, 64>(probs, count, max_m, ncb, stream)
-                   : launch_bits_g<1, 128>(probs, count, max_m, ncb, stream);
+    switch (g) {
+        case 32: return launch_bits_g<1, 32>(probs, count, max_m, ncb, stream);
+        case 64: return launch_bits_g<1, 64>(probs, count, max_m, ncb, stream);
+        default: return launch_bits_g<1, 128>(probs, count, max_m, ncb, stream);
+    }
 }
 
 hipError_t launch_gemm_skinny(const GemmProblem& p, int g, int bits, hipStream_t stream) {

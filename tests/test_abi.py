@@ -117,18 +117,18 @@ def test_variant_choice():
 
 
 def test_skinny_variant_choice():
-    """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) for g = 64 / 128 when K
-    is a whole number of 64-byte row steps (a binary chunk of 128 codes spans two groups of
-    64; the kernel runs each of its MFMAs once per group)."""
+    """The skinny kernel takes M <= 32 (ternary) / M <= 16 (binary) for g = 32 / 64 / 128 when
+    K is a whole number of 64-byte row steps (a 16-byte chunk larger than a group -- 64
+    ternary or 128 binary codes -- runs each of its MFMAs once per group)."""
     assert lb.variant(16, 3072, 3072, 64, 2) == "skinny"
     assert lb.variant(1, 3072, 3072, 128, 2) == "skinny"
     assert lb.variant(32, 3072, 12288, 64, 2) == "skinny"
     assert lb.variant(33, 3072, 3072, 64, 2) == "tile64x256"
-    assert lb.variant(16, 3072, 3072, 32, 2) == "tile64x256"     # group of 32 < chunk of 64
+    assert lb.variant(16, 3072, 3072, 32, 2) == "skinny"         # chunk of 64 over two groups
     assert lb.variant(16, 3072, 320, 64, 2) == "tile64x256"      # K % 256 != 0
     assert lb.variant(16, 3072, 3072, 128, 1) == "skinny"
     assert lb.variant(16, 3072, 3072, 64, 1) == "skinny"         # binary chunk over two groups
-    assert lb.variant(16, 3072, 3072, 32, 1) == "tile64x256"     # group of 32
+    assert lb.variant(16, 3072, 3072, 32, 1) == "skinny"         # ... or four
     assert lb.variant(16, 3072, 2816, 128, 1) == "tile64x256"    # K % 512 != 0
     assert lb.variant(17, 3072, 3072, 128, 1) == "tile64x256"
 

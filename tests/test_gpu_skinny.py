@@ -45,7 +45,7 @@ def _is_zero(bits):
 
 
 # (bits, g, K): K = 5 row steps, so the four waves get 1, 1, 1 and 2 steps
-_FORMATS = [(2, 64, 1280), (2, 128, 1280), (1, 128, 2560), (1, 64, 2560)]
+_FORMATS = [(2, 64, 1280), (2, 128, 1280), (1, 128, 2560), (1, 64, 2560), (2, 32, 1280), (1, 32, 2560)]
 
 
 @pytest.mark.parametrize("bits,g,K", _FORMATS)
@@ -56,14 +56,14 @@ def test_every_stripe_width(bits, g, K, ncb, monkeypatch):
 
 
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 31, 32])
-@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("g", [32, 64, 128])
 def test_rows(M, g):
     # 65 column blocks: only one-block stripes divide N
     _check(M, 1040, 768, g, 2, seed=1, what="rows")
 
 
 @pytest.mark.parametrize("M", [1, 9, 16])
-@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("g", [32, 64, 128])
 def test_rows_binary(M, g):
     _check(M, 1040, 1536, g, 1, seed=2, what=f"rows binary g{g}")
 
@@ -74,7 +74,7 @@ def test_step_counts(K):
     _check(16, 512, K, 64, 2, seed=3, what="steps")
 
 
-@pytest.mark.parametrize("bits,g", [(2, 64), (2, 128), (1, 128), (1, 64)])
+@pytest.mark.parametrize("bits,g", [(2, 64), (2, 128), (1, 128), (1, 64), (2, 32), (1, 32)])
 def test_one_hot_bit_exact(bits, g):
     M, N, K = 16, 64, 1024
     x = W.gen_x(W.rng_for(4, 41, 0), M, K)
@@ -121,7 +121,7 @@ def test_zero_codes_scales_and_unused_field():
     assert not y.float().abs().sum().item()
 
 
-@pytest.mark.parametrize("bits,g", [(2, 64), (1, 128), (1, 64)])
+@pytest.mark.parametrize("bits,g", [(2, 64), (1, 128), (1, 64), (2, 32), (1, 32)])
 def test_linearity_bit_exact(bits, g):
     M, N, K = 16, 512, 2048
     inp = _inputs(M, N, K, g, bits, seed=6)
