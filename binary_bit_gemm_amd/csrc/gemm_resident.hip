@@ -124,10 +124,19 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     const int s_copies = (CB * 16 * dpr + 63) / 64;
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.S, uint32_t(N) * s_row);
     const uint32_t s_src = uint32_t(group * CB * 16) * s_row + uint32_t(kb * GPS) * 2u;
-    for (int j = wave; j < s_copies; j += nwaves) {
-        const int d = 64 * j + lane;
-        const int r = d / dpr, k = d - r * dpr;
-        dma4(sr, lds + s_base + 256 * j, s_src + uint32_t(r) * s_row + uint32_t(k) * 4u);
+    if (tw == T) {
+        // whole K: the workgroup's rows of scales are one contiguous block of CB * 16 * s_row
+        // bytes (a multiple of 16, at a multiple of 16); 16-byte copies, a quarter of the
+        // instructions of the row-by-row 4-byte copies below (the region is rounded up to
+        // 1 KB, so the last copy fits; past the buffer's end it reads zeros)
+        const int s16 = (CB * 16 * int(s_row) + 1023) / 1024;
+        for (int j = wave; j < s16; j += nwaves) dma16(sr, lds + s_base + 1024 * j, s_src + 1024u * uint32_t(j) + 16u * uint32_t(lane), 0);
+    } else {
+        for (int j = wave; j < s_copies; j += nwaves) {
+            const int d = 64 * j + lane;
+            const int r = d / dpr, k = d - r * dpr;
+            dma4(sr, lds + s_base + 256 * j, s_src + uint32_t(r) * s_row + uint32_t(k) * 4u);
+        }
     }
     // the counted wait below relies on these copies preceding the weight loads
     asm volatile("" ::: "memory");
