@@ -7,7 +7,11 @@
 // 288 x 192 tile (12 waves of 96 x 48): 4608 x 3072 is then exactly 256 tiles, 4608 x 9216
 // and 4608 x 18432 whole multiples of 256.  Per FLOP the 16x16x32 instruction needs the same
 // operand bytes, the same code expansion and the same scale FMAs as the 32x32x16 one.  The
-// same kernel with 4 waves makes a 96 x 192 tile: 1536 x 3072 is then exactly 256 tiles.
+// same kernel with 4 waves makes a 96 x 192 tile: 1536 x 3072 is then exactly 256 tiles.  There
+// one wave per SIMD leaves the SIMD idle whenever its wave waits, so that tile also comes with
+// its K range split between KSPLIT groups of 4 waves: each group streams its own half of K
+// through its own LDS buffers (the groups share the step barrier), and at the end the groups'
+// fp32 sums are added in group order 0, 1 (a fixed order) before the epilogue.
 //
 // Data movement is that of the 32x32 kernel (direct-to-LDS copies of X per 64-element step,
 // of packed weights in 64-byte row blocks, of scales in 8-group blocks; everything
@@ -47,7 +51,7 @@ __device__ __forceinline__ int w_pos(int row, int chunk) { return chunk ^ ((row 
 
 template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg16 {
-    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int WAVES = WAVES_M * WAVES_N;  // of one K group
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int MB = WM / 16, NB = WN / 16;
@@ -65,18 +69,30 @@ struct Cfg16 {
     static_assert(BITS == 1 || BITS == 2, "binary or ternary codes");
 };
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(ProblemGroup grp) {
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp) {
     using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
     constexpr int kWSpb = C::W_SPB;
-    __shared__ __attribute__((aligned(16))) unsigned char xa0[C::X_TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char xa1[C::X_TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char wk0[C::W_BLOCK];
-    __shared__ __attribute__((aligned(16))) unsigned char wk1[C::W_BLOCK];
-    __shared__ __attribute__((aligned(16))) unsigned char sk0[C::S_BLOCK];
-    __shared__ __attribute__((aligned(16))) unsigned char sk1[C::S_BLOCK];
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && C::WAVES == 4), "K groups of 4 waves, two of them");
+    // One set of buffers per K group.  Separate static arrays per buffer role (not one array
+    // indexed by parity): the compiler can then see that reads of one buffer do not depend on
+    // copies still landing in the other.
+    __shared__ __attribute__((aligned(16))) unsigned char xa0_[KSPLIT][C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char xa1_[KSPLIT][C::X_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char wk0_[KSPLIT][C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char wk1_[KSPLIT][C::W_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk0_[KSPLIT][C::S_BLOCK];
+    __shared__ __attribute__((aligned(16))) unsigned char sk1_[KSPLIT][C::S_BLOCK];
 
-    const int tid = threadIdx.x;
+    // K group kg (wave-uniform) and the thread's index inside it
+    const int kg = KSPLIT == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) / C::THREADS);
+    unsigned char* const xa0 = xa0_[kg];
+    unsigned char* const xa1 = xa1_[kg];
+    unsigned char* const wk0 = wk0_[kg];
+    unsigned char* const wk1 = wk1_[kg];
+    unsigned char* const sk0 = sk0_[kg];
+    unsigned char* const sk1 = sk1_[kg];
+    const int tid = int(threadIdx.x) - kg * C::THREADS;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -96,6 +112,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
 
     const int kgroups = K / G;
     const int ksteps = K / KS;
+    // the group's steps [kbeg, kend); every group has the same count (the host sends KSPLIT = 2
+    // only for an even step count), so all run the same barriers
+    const int kbeg = kg * (ksteps / KSPLIT), kend = kbeg + ksteps / KSPLIT;
     const uint32_t w_row_bytes = uint32_t(K) * BITS / 8u;
     const uint32_t s_row_bytes = uint32_t(kgroups) * 2u;
 
@@ -280,17 +299,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
     const int s_blocks = (kgroups + kSGpb - 1) / kSGpb;
 
     auto prefetch_x = [&](int step, unsigned char* xbuf) {
-        if (step + 1 < ksteps) issue_x(step + 1, xbuf);
+        if (step + 1 < kend) issue_x(step + 1, xbuf);
     };
+    // The next weight (scale) block is copied on the first step of a block and on the group's
+    // first step, which can fall inside a block.
     auto prefetch_blocks = [&](int step) {
-        if (step % kWSpb == 0 && step / kWSpb + 1 < w_blocks) issue_w(step / kWSpb + 1, w_buf(step + kWSpb));
+        const int wb = step / kWSpb;
+        if ((step == kbeg || step % kWSpb == 0) && wb + 1 < w_blocks && (wb + 1) * kWSpb < kend)
+            issue_w(wb + 1, ((wb + 1) & 1) ? wk1 : wk0);
         const int sb = s_block(step);
-        if ((step == 0 || s_block(step - 1) != sb) && sb + 1 < s_blocks) issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+        if ((step == kbeg || s_block(step - 1) != sb) && sb + 1 < s_blocks && s_block(kend - 1) > sb)
+            issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
     };
 
-    issue_x(0, xa0);
-    issue_w(0, wk0);
-    issue_s(0, sk0);
+    issue_x(kbeg, xa0);
+    issue_w(kbeg / kWSpb, w_buf(kbeg));
+    issue_s(s_block(kbeg), s_buf(kbeg));
     wait_vmcnt0();
     __syncthreads();
 
@@ -299,9 +323,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
     // of an iteration made the register allocator give every accumulator a second register
     // and copy it back each iteration.
     Ops ops;
-    int step = 0;
+    int step = kbeg;
 #pragma nounroll
-    for (; step + 1 < ksteps; step += 2) {
+    for (; step + 1 < kend; step += 2) {
         read_operands(w_buf(step), s_buf(step), step, ops);
         prefetch_x(step, xa1);
         prefetch_blocks(step);
@@ -315,9 +339,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
         wait_vmcnt0();
         __syncthreads();
     }
-    if (step < ksteps) {
+    if (step < kend) {
         read_operands(w_buf(step), s_buf(step), step, ops);
         compute(xa0, ops);
+    }
+
+    // ---- K groups: group 1's sums through LDS, added to group 0's (order 0, 1) ----
+    if constexpr (KSPLIT == 2) {
+        __syncthreads();  // every read of the last step is done: the buffers are free
+        // A wave's sums (MB x NB blocks of 64 lanes x 16 bytes, 18 KB at 96 x 48) go to the
+        // wave's buffer role (wave 0: X buffer 0, 1: X buffer 1, 2 and 3: weight buffers 0 and 1)
+        // of both sets: blocks [0, kPer) into group 0's, the rest into group 1's.
+        constexpr int kPer = C::X_TILE / 1024;
+        static_assert(C::X_TILE == C::W_BLOCK && C::MB * C::NB <= 2 * kPer, "a wave's sums fit two buffers");
+        unsigned char* const r0 = wave_u == 0 ? xa0_[0] : wave_u == 1 ? xa1_[0] : wave_u == 2 ? wk0_[0] : wk1_[0];
+        unsigned char* const r1 = wave_u == 0 ? xa0_[1] : wave_u == 1 ? xa1_[1] : wave_u == 2 ? wk0_[1] : wk1_[1];
+        auto slot = [&](int b) {
+            return reinterpret_cast<f32x4_t*>(b < kPer ? r0 + 1024 * b : r1 + 1024 * (b - kPer)) + lane;
+        };
+        if (kg == 1) {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) *slot(mb * C::NB + nb) = acc[mb][nb];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const f32x4_t u = *slot(mb * C::NB + nb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][nb][i] += u[i];
+            }
     }
 
     // ---- epilogue ----
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tile16_kernel(
     }
 }
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1>
 hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
     ProblemGroup grp{};
     int total = 0;
@@ -373,8 +428,8 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
         grp.tile_end[i] = total;
     }
     grp.count = count;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N>), dim3(total), dim3(64 * WAVES_M * WAVES_N),
-                       0, stream, grp);
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT>), dim3(total),
+                       dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
     return hipGetLastError();
 }
 
@@ -386,6 +441,14 @@ template <int G, int BITS>
 hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hipStream_t stream) {
     // 288 x 192 in 12 waves of 96 x 48: LDS 72 KB (X) + 24 KB (W) + 12 KB (S).
     // 96 x 192 in 4 waves of 96 x 48 (LDS 60 KB): 1536 x 3072 outputs are exactly 256 tiles.
+    // With K split between two groups of 4 waves (LDS 120 KB) where every problem has an even
+    // number of 64-element steps.
+    if (variant == TILE_96x192K2) {
+        bool even = true;
+        for (int i = 0; i < count; ++i) even = even && (probs[i].K / KS) % 2 == 0;
+        if (even) return launch_cfg16<G, BITS, 96, 192, 1, 4, 2>(probs, count, stream);
+        return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
+    }
     if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
     return launch_cfg16<G, BITS, 288, 192, 3, 4>(probs, count, stream);
 }

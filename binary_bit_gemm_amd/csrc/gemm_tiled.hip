@@ -372,13 +372,18 @@ struct TileShape {
 // ~0.82 (binary) of a 256 x 256 tile's work per unit time (smaller wave tiles: less operand
 // reuse), which about cancels (ternary) or outweighs (binary) the 16% of units a 256 x 256
 // grid leaves idle at N = 3072.  A 96 x 192 tile (four waves, one per SIMD) does ~0.54; it
-// pays where nothing larger fills the chip (1536 x 3072: 256 tiles).
+// pays where nothing larger fills the chip (1536 x 3072: 256 tiles).  The same tile with K
+// split between two groups of four waves does ~0.65 where the grid is a single round (one
+// workgroup per compute unit: 1536 x 3072 at K = 3072 and 9216 measured 17% and 21% faster);
+// over several rounds two plain 96 x 192 workgroups share a compute unit instead, and the
+// split measured slower.
 constexpr TileShape kTiles[] = {
     {TILE_256x256, 256, 256, 1, 1.00f, 1.00f},
     {TILE_288x192, 288, 192, 1, 0.87f, 0.82f},
     {TILE_128x256, 128, 256, 2, 0.92f, 0.92f},
     {TILE_64x256, 64, 256, 2, 0.75f, 0.75f},
     {TILE_96x192, 96, 192, 1, 0.54f, 0.51f},
+    {TILE_96x192K2, 96, 192, 1, 0.65f, 0.62f},
 };
 
 }  // namespace
@@ -388,16 +393,20 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
     double best_cost = 0.0;
     for (const TileShape& t : kTiles) {
         if (is_tile16_variant(t.variant) && !tile16_supported(g, bits)) continue;
-        if (t.variant == TILE_96x192) {  // measured at M = 1536; below M = 1024 it stays unused
-            bool small = false;
-            for (int i = 0; i < count; ++i) small = small || probs[i].M < 1024;
-            if (small) continue;
+        if (t.variant == TILE_96x192 || t.variant == TILE_96x192K2) {
+            // measured at M = 1536; below M = 1024 they stay unused.  The K split needs an even
+            // number of 64-element steps.
+            bool skip = false;
+            for (int i = 0; i < count; ++i)
+                skip = skip || probs[i].M < 1024 || (t.variant == TILE_96x192K2 && (probs[i].K / 64) % 2 != 0);
+            if (skip) continue;
         }
         int64_t tiles = 0;
         for (int i = 0; i < count; ++i)
             tiles += int64_t((probs[i].M + t.bm - 1) / t.bm) * ((probs[i].N + t.bn - 1) / t.bn);
         const int64_t slots = int64_t(kComputeUnits) * t.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
+        if (t.variant == TILE_96x192K2 && rounds > 1) continue;  // single rounds only (see above)
         const double cost = double(rounds) * t.per_cu * t.bm * t.bn / (bits == 1 ? t.eff_binary : t.eff);
         if (best_cost == 0.0 || cost < best_cost) {
             best = t.variant;
@@ -419,6 +428,7 @@ const char* tile_variant_name(int variant) {
         case TILE_128x256: return "tile128x256";
         case TILE_288x192: return "tile288x192";
         case TILE_96x192: return "tile96x192";
+        case TILE_96x192K2: return "tile96x192k2";
         default: return "tile64x256";
     }
 }

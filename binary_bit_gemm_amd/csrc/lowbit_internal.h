@@ -34,9 +34,10 @@ hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K,
 // Tiled MFMA kernels (LDS-staged X, packed weights and scales).  `variant` selects the tile;
 // TILE_288x192 and TILE_96x192 are the 16x16x32-block kernel (g = 64 or 128 only).
 enum TileVariant {
-    TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5
+    TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5,
+    TILE_96x192K2 = 6  // 96 x 192 with K split between two groups of 4 waves (even step counts)
 };
-inline bool is_tile16_variant(int v) { return v == TILE_288x192 || v == TILE_96x192; }
+inline bool is_tile16_variant(int v) { return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2; }
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.

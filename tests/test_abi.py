@@ -108,11 +108,13 @@ def test_variant_choice():
     assert lb.variant(4608, 3072, 12288, 128, 1) == "tile256x256"
     assert lb.variant(4608, 3072, 3072, 32, 2) == "tile256x256"
     assert lb.variant(4608, 3072, 3072, 32, 1) == "tile256x256"
-    # M = 1536: 96 x 192 tiles fill the chip at N = 3072 (256 tiles), 256 x 256 wins above
-    assert lb.variant(1536, 3072, 3072, 64, 2) == "tile96x192"
-    assert lb.variant(1536, 3072, 9216, 64, 1) == "tile96x192"
+    # M = 1536: 96 x 192 tiles fill the chip at N = 3072 (256 tiles, one round), with K split
+    # between two groups of waves where the step count is even; 256 x 256 wins above
+    assert lb.variant(1536, 3072, 3072, 64, 2) == "tile96x192k2"
+    assert lb.variant(1536, 3072, 9216, 64, 1) == "tile96x192k2"
+    assert lb.variant(1536, 3072, 3136, 64, 2) == "tile96x192"  # 49 steps
     assert lb.variant(1536, 9216, 3072, 64, 2) == "tile256x256"
-    assert lb.variant(1536, 3072, 3072, 32, 2) != "tile96x192"  # g = 32: 32x32-block kernel only
+    assert not lb.variant(1536, 3072, 3072, 32, 2).startswith("tile96")  # g = 32: 32x32-block kernel only
     assert lb.variant(64, 256, 256, 64, 2).startswith("tile")
 
 

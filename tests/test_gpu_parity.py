@@ -102,7 +102,7 @@ def test_gemm_small(M, N, K, g, bits):
     _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{M}x{N}x{K} g{g} b{bits}")
 
 
-@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "tile288", "tile96", "skinny"])
+@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "tile288", "tile96", "tile96k2", "skinny"])
 @pytest.mark.parametrize("M", [16, 300, 600])
 def test_every_variant(variant, M, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
@@ -113,7 +113,7 @@ def test_every_variant(variant, M, monkeypatch):
             _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{variant} M={M} g{g} b{bits}")
 
 
-@pytest.mark.parametrize("variant", ["tile288", "tile96"])
+@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2"])
 @pytest.mark.parametrize("bits", [2, 1])
 @pytest.mark.parametrize("M,N,K,g", [(600, 400, 1280, 64), (300, 592, 3072, 128), (289, 208, 64, 64),
                                      (577, 192, 8448, 128)])
@@ -123,10 +123,27 @@ def test_tile16_several_blocks(M, N, K, g, bits, variant, monkeypatch):
     # runs past the row (K % 512 != 0 for binary), a single step, and ragged tiles in both
     # directions
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
-    assert lb.variant(M, N, K, g, bits) == {"tile288": "tile288x192", "tile96": "tile96x192"}[variant]
+    assert lb.variant(M, N, K, g, bits) == {"tile288": "tile288x192", "tile96": "tile96x192",
+                                            "tile96k2": "tile96x192k2"}[variant]
     inp = _inputs(M, N, K, g, bits, seed=11)
     y, _ = run_gemm(inp, g, bits)
     _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{variant} {M}x{N}x{K} g{g} b{bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 1])
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("K", [128, 256, 384, 640, 1536, 2304])
+def test_tile96_k_groups(K, g, bits, monkeypatch):
+    # 96 x 192 with K split between two groups of waves: each group's range starts at step
+    # K / 128 (inside a weight block of 4 ternary / 8 binary steps, or a scale block, for most
+    # of these K), one step per group (K = 128) up to 18; ragged tiles in both directions
+    if K % g:
+        pytest.skip("K must be a multiple of g")
+    monkeypatch.setenv("LOWBIT_VARIANT", "tile96k2")
+    M, N = 200, 400
+    inp = _inputs(M, N, K, g, bits, seed=13)
+    y, _ = run_gemm(inp, g, bits)
+    _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"tile96k2 {M}x{N}x{K} g{g} b{bits}")
 
 
 def test_empty_and_k0():
