@@ -189,7 +189,7 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
