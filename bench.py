@@ -90,7 +90,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
-                    choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny"])
+                    choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -119,7 +119,16 @@ def problems_for(workload):
         return W.denoise_step_sweep()
     if workload == "skinny":
         return W.denoise_step_sweep(skinny_m=16)
+    if workload == "swiglu":
+        # the MLP-in linear at 1024^2 (M = 4608, [gate | up] = 2 x 9216 weight rows, K = 3072) with
+        # its SwiGLU fused: Y is [4608, 9216]
+        return [W.Problem("m4608_mlp_in_swiglu", 4608, 18432, 3072, W.TERNARY, 64, 3, 2)]
     raise ValueError(workload)
+
+
+def swiglu_bytes(p):
+    """Algorithmic bytes of a fused SwiGLU problem: Y has half the columns of the weight rows."""
+    return p.bytes_moved() - p.M * (p.N // 2) * 2
 
 
 def make_device_inputs(probs, seed):
@@ -146,7 +155,7 @@ def make_device_inputs(probs, seed):
     return bufs
 
 
-def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0):
+def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=False):
     """The oracle as it stands (unpack, fp64 dequantise, numpy matmul) on the first `rows`
     rows of X for every distinct shape of the workload, on the host's cores, in the unit of
     the metric (TFLOP/s of 2*M*N*K, or GB/s of the algorithmic bytes of the sampled GEMMs)."""
@@ -174,10 +183,13 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0):
     while passes == 0 or elapsed < min_seconds:
         for q, inp, words in cases:
             t0 = time.perf_counter()
-            oracle.gemm_ref_from_words(inp.x, words, inp.scales, q.K, q.g, q.bits)
+            if swiglu:
+                oracle.swiglu_ref_f64(inp.x, oracle.unpack(words, q.K, q.bits), inp.scales, q.g)
+            else:
+                oracle.gemm_ref_from_words(inp.x, words, inp.scales, q.K, q.g, q.bits)
             elapsed += time.perf_counter() - t0
             flops += 2 * q.M * q.N * q.K
-            nbytes += q.bytes_moved()
+            nbytes += swiglu_bytes(q) if swiglu else q.bytes_moved()
         passes += 1
     value = flops / elapsed / 1e12 if unit == "TFLOP/s" else nbytes / elapsed / 1e9
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
@@ -208,6 +220,10 @@ def main():
     probs = problems_for(a.workload)
     groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
     bufs = make_device_inputs(probs, a.seed)
+    swiglu = a.workload == "swiglu"
+    if swiglu:  # the fused SwiGLU writes half the columns
+        x, w, s, _, g, bits = bufs[0]
+        bufs[0] = (x, w, s, torch.empty((x.shape[0], w.shape[0] // 2), dtype=torch.bfloat16, device="cuda"), g, bits)
 
     # one caller workspace (zero-filled once, reused by every call: each call leaves its
     # counters at zero) for the calls that split K across workgroups
@@ -221,7 +237,10 @@ def main():
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need > 0 else None
 
     def launch(grp):
-        if len(grp) == 1:
+        if swiglu:
+            x, w, s, y, g, bits = bufs[grp[0]]
+            lb.gemm_swiglu(x, w, s, g, bits, out=y)
+        elif len(grp) == 1:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm(x, w, s, g, bits, out=y, workspace=ws)
         else:
@@ -279,7 +298,7 @@ def main():
                for i in range(len(groups))]
 
     flops_step = sum(p.flops for p in probs)
-    bytes_step = sum(p.bytes_moved() for p in probs)
+    bytes_step = sum(swiglu_bytes(p) if swiglu else p.bytes_moved() for p in probs)
     ms_per_step = elapsed * 1e3 / a.steps
     tflops = flops_step / (elapsed / a.steps) / 1e12
     launches = len(groups)
@@ -321,7 +340,7 @@ def main():
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed, unit, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(probs, a.cpu_rows, a.seed, unit, a.cpu_seconds, swiglu=swiglu)
     print(json.dumps(out), flush=True)
 
 

@@ -140,6 +140,35 @@ class Problem(ctypes.Structure):
                 ("g", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
+def gemm_swiglu(x, words, scales, g: int, bits: int, out=None):
+    """Y[M, N] = silu(X . dequant(Wg)^T) * (X . dequant(Wu)^T) in bf16, with `words` / `scales`
+    holding 2N rows: gate rows [0, N), then up rows [N, 2N) (lowbit_gemm_swiglu)."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    _require(words, torch.int32, "words")
+    _require(scales, torch.float16, "scales")
+    M, K = x.shape
+    N2 = words.shape[0]
+    if N2 % 2:
+        raise ValueError(f"words must hold 2N rows (gate then up), got {N2}")
+    N = N2 // 2
+    if words.shape[1] != words_per_row(K, bits):
+        raise ValueError(f"words must be [2N, K*bits/32] = [{N2}, {words_per_row(K, bits)}], got {tuple(words.shape)}")
+    if K % g or tuple(scales.shape) != (N2, K // g):
+        raise ValueError(f"scales must be [2N, K/g] = [{N2}, {K // g if g else 0}], got {tuple(scales.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().lowbit_gemm_swiglu(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
+    _check(st, "lowbit_gemm_swiglu")
+    return out
+
+
 def _problem_array(problems):
     torch = _torch()
     if len(problems) > MAX_BATCH:

@@ -69,11 +69,17 @@ struct Cfg16 {
     static_assert(BITS == 1 || BITS == 2, "binary or ternary codes");
 };
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT>
+// SWIGLU: the problem's W and S hold 2N rows, gate rows [0, N) then up rows [N, 2N), and Y[M, N] =
+// silu(X . Wgate^T) * (X . Wup^T), both factors taken from the fp32 sums and rounded to bf16 once.
+// A wave's two 16-column blocks are then the gate and the up rows of the same 16 output columns,
+// so the epilogue combines them in registers; a BN-row weight tile makes BN / 2 output columns.
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, bool SWIGLU = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp) {
     using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
     constexpr int kWSpb = C::W_SPB;
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && C::WAVES == 4), "K groups of 4 waves, two of them");
+    static_assert(!SWIGLU || (C::NB == 2 && KSPLIT == 1), "gate and up block per wave");
+    constexpr int kOutBn = SWIGLU ? BN / 2 : BN;  // output columns per tile
     // One set of buffers per K group.  Separate static arrays per buffer role (not one array
     // indexed by parity): the compiler can then see that reads of one buffer do not depend on
     // copies still landing in the other.
@@ -105,9 +111,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     const GemmProblem p = grp.p[pi];
     const int tile = t - (pi > 0 ? grp.tile_end[pi - 1] : 0);
     const int M = p.M, N = p.N, K = p.K;
-    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles_n = (N + kOutBn - 1) / kOutBn;
     const int tm = tile / tiles_n, tn = tile % tiles_n;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * kOutBn;
+    // Global weight row of the tile's weight row r (rows past the last output column re-read a
+    // valid row; their results are not stored).  SwiGLU: row r = 32 w + 16 h + i is output
+    // column n0 + 16 w + i, of the gate (h = 0) or the up (h = 1) half.
+    const int w_rows = SWIGLU ? 2 * N : N;
+    auto wrow = [&](int r) {
+        if constexpr (SWIGLU) {
+            const int c = n0 + 16 * (r >> 5) + (r & 15);
+            return (c < N ? c : N - 1) + ((r >> 4) & 1) * N;
+        } else {
+            const int n = n0 + r;
+            return n < N ? n : N - 1;
+        }
+    };
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
 
     const int kgroups = K / G;
@@ -139,7 +158,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     // ---- packed weights: block b = steps [b W_SPB, (b+1) W_SPB) of the tile's BN rows, 64 bytes per row.
     // Copy slot s = row s / 4, stored position s % 4 (holding source chunk w_pos(row, s % 4)).
     // Rows past N re-read row N-1.
-    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(N) * w_row_bytes);
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(w_rows) * w_row_bytes);
     auto issue_w = [&](int block, unsigned char* buf) {
 #pragma unroll
         for (int i = 0; i < (C::W_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
@@ -147,8 +166,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             if (slot0 < C::W_SLOTS) {
                 const int slot = slot0 + lane;
                 const int r = slot >> 2;
-                int n = n0 + r;
-                n = n < N ? n : N - 1;
+                const int n = wrow(r);
                 const uint32_t voff = uint32_t(n) * w_row_bytes + uint32_t(w_pos(r, slot & 3) * 16);
                 dma16(w_rs, buf + slot0 * 16, voff, __builtin_amdgcn_readfirstlane(block * kWB));
             }
@@ -157,7 +175,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 
     // ---- scales: block b = groups [8b, 8b+8) of the tile's BN rows, as two aligned 16-byte
     // windows per row; the row's group 8b sits (row offset & 15) bytes in.
-    const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(p.S, uint32_t(N) * s_row_bytes);
+    const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(p.S, uint32_t(w_rows) * s_row_bytes);
     auto issue_s = [&](int block, unsigned char* buf) {
 #pragma unroll
         for (int i = 0; i < (C::S_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
@@ -165,8 +183,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             if (slot0 < C::S_SLOTS) {
                 const int slot = slot0 + lane;
                 const int r = slot >> 1;
-                int n = n0 + r;
-                n = n < N ? n : N - 1;
+                const int n = wrow(r);
                 const uint32_t start = uint32_t(n) * s_row_bytes + uint32_t(block) * 16u;
                 const uint32_t voff = (start & ~15u) + uint32_t(slot & 1) * 16u;
                 dma16(s_rs, buf + slot0 * 16, voff, 0);
@@ -186,8 +203,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
         const int r = wn0 + nb * 16 + l16;
-        int n = n0 + r;
-        n = n < N ? n : N - 1;
+        const int n = wrow(r);
         w_rd[nb] = r * kWB + (BITS == 2 ? 8 * (q >> 1) : 0);
         s_rd[nb] = r * 32 + int((uint32_t(n) * s_row_bytes) & 15u);
     }
@@ -395,40 +411,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     auto pack = [](float lo, float hi) {
         return uint32_t(float_to_bf16_bits(lo)) | (uint32_t(float_to_bf16_bits(hi)) << 16);
     };
+    // one 16x16 block of fp32 results to bf16 at columns nblk .. nblk + 15 of row block mb
+    auto store_block = [&](const f32x4_t& a, int nblk, int mb) {
+        if (nblk >= N) return;  // N % 16 == 0: a block is in or out as a whole
+        const uint32_t P = pack(a[0], a[1]);  // rows 0, 1 of column b4
+        const uint32_t Q = pack(a[2], a[3]);  // rows 2, 3
+        const uint32_t own = lower_pair ? P : Q;
+        const uint32_t got =
+            uint32_t(__builtin_amdgcn_update_dpp(0, int(lower_pair ? Q : P), kQuadSwap2, 0xF, 0xF, true));
+        const uint32_t E = lower_pair ? own : got, F = lower_pair ? got : own;
+        const uint32_t R =
+            uint32_t(__builtin_amdgcn_update_dpp(0, int(perm_b32(F, E, send_sel)), kQuadSwap1, 0xF, 0xF, true));
+        const uint32_t d0 = perm_b32(R, E, d0_sel), d1 = perm_b32(R, F, d1_sel);
+        const int m = m0 + wm0 + mb * 16 + 4 * q + b4;
+        if (m < M) {
+            *reinterpret_cast<u32x2_t*>(p.Y + int64_t(m) * N + nblk + (l16 & ~3)) = u32x2_t{d0, d1};
+        }
+    };
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
+        if constexpr (SWIGLU) {
+            // silu(g) * u = g * u / (1 + exp(-g)); exp overflows to inf for very negative g and
+            // the quotient goes to -0, the limit
+            f32x4_t y;
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            const int nblk = n0 + wn0 + nb * 16;
-            if (nblk >= N) continue;  // N % 16 == 0: a block is in or out as a whole
-            const uint32_t P = pack(acc[mb][nb][0], acc[mb][nb][1]);  // rows 0, 1 of column b4
-            const uint32_t Q = pack(acc[mb][nb][2], acc[mb][nb][3]);  // rows 2, 3
-            const uint32_t own = lower_pair ? P : Q;
-            const uint32_t got = uint32_t(
-                __builtin_amdgcn_update_dpp(0, int(lower_pair ? Q : P), kQuadSwap2, 0xF, 0xF, true));
-            const uint32_t E = lower_pair ? own : got, F = lower_pair ? got : own;
-            const uint32_t R = uint32_t(
-                __builtin_amdgcn_update_dpp(0, int(perm_b32(F, E, send_sel)), kQuadSwap1, 0xF, 0xF, true));
-            const uint32_t d0 = perm_b32(R, E, d0_sel), d1 = perm_b32(R, F, d1_sel);
-            const int m = m0 + wm0 + mb * 16 + 4 * q + b4;
-            if (m < M) {
-                *reinterpret_cast<u32x2_t*>(p.Y + int64_t(m) * N + nblk + (l16 & ~3)) = u32x2_t{d0, d1};
+            for (int i = 0; i < 4; ++i) {
+                const float gt = acc[mb][0][i];
+                y[i] = gt * acc[mb][1][i] / (1.0f + __expf(-gt));
             }
+            store_block(y, n0 + 16 * wave_n, mb);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) store_block(acc[mb][nb], n0 + wn0 + nb * 16, mb);
         }
     }
 }
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, bool SWIGLU = false>
 hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
     ProblemGroup grp{};
     int total = 0;
+    constexpr int kOutBn = SWIGLU ? BN / 2 : BN;
     for (int i = 0; i < count; ++i) {
         grp.p[i] = probs[i];
-        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + BN - 1) / BN);
+        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + kOutBn - 1) / kOutBn);
         grp.tile_end[i] = total;
     }
     grp.count = count;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT>), dim3(total),
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, SWIGLU>), dim3(total),
                        dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
     return hipGetLastError();
 }
@@ -454,6 +484,17 @@ hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hi
     }
     if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
     return launch_cfg16<G, BITS, 288, 192, 2, 6>(probs, count, stream);
+}
+
+template <int G, int BITS>
+hipError_t launch_swiglu16(const GemmProblem* probs, int count, hipStream_t stream) {
+    return launch_cfg16<G, BITS, 288, 192, 2, 6, 1, true>(probs, count, stream);
+}
+
+hipError_t launch_gemm_tile16_swiglu(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
+    if (count < 1 || count > kMaxGroup || !tile16_supported(g, bits)) return hipErrorInvalidValue;
+    if (bits == 2) return g == 64 ? launch_swiglu16<64, 2>(probs, count, stream) : launch_swiglu16<128, 2>(probs, count, stream);
+    return g == 64 ? launch_swiglu16<64, 1>(probs, count, stream) : launch_swiglu16<128, 1>(probs, count, stream);
 }
 
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,

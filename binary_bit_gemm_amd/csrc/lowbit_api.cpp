@@ -255,6 +255,29 @@ int lowbit_gemm(const void* X, const uint32_t* W, const void* S, void* Y,
     return launch_one(p, g, bits, static_cast<hipStream_t>(stream));
 }
 
+int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y, int64_t M, int64_t N, int64_t K,
+                       int g, int bits, void* stream) {
+    if (N < 0 || N > kMaxDim / 2) return LOWBIT_E_INVALID;
+    // the weight side has 2N rows; Y has N columns (checked against 2N outputs: stricter)
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, 2 * N, K, g, bits);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    if (!lowbit::tile16_supported(g, bits)) return LOWBIT_E_UNSUPPORTED;
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                          static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
+    hipError_t e;
+    if (K == 0) {  // silu(0) * 0
+        const int64_t n = M * N;
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p.Y, n);
+        e = hipGetLastError();
+    } else {
+        e = lowbit::launch_gemm_tile16_swiglu(&p, 1, g, bits, s);
+    }
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
 size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits) {
     if (lowbit_check_gemm_args(nullptr, nullptr, nullptr, nullptr, 0, N, K, g, bits) != LOWBIT_OK) return 0;
     if (M <= 0 || N <= 0 || K <= 0) return 0;

@@ -79,6 +79,9 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits);
 int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
 const char* tile_variant_name(int variant);
 bool tile16_supported(int g, int bits);
+// Fused SwiGLU on the 288 x 192 16x16-block tile: each problem's W and S hold 2N rows (gate
+// rows [0, N), up rows [N, 2N)), Y is [M, N].
+hipError_t launch_gemm_tile16_swiglu(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                     hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);

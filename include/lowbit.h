@@ -152,6 +152,22 @@ size_t lowbit_batched_workspace_size(const lowbit_problem* problems, int count);
 int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * lowbit_gemm_swiglu -- the MLP-in linear with its SwiGLU gate fused into the epilogue:
+ *   Y[M, N] = silu(X . dequant(Wg)^T) * (X . dequant(Wu)^T),  silu(a) = a / (1 + exp(-a)),
+ * where W / S hold 2N rows: gate rows Wg = rows [0, N), up rows Wu = rows [N, 2N) (the
+ * MMDiT's MLP-in linear of 2 x 9216 outputs in the mlx page's component architecture; which
+ * half gates is not stated there -- gate first is this library's reading).
+ *   X  device bf16 [M, K];  W  device packed words [2N, K*bits/32];
+ *   S  device fp16 [2N, K/g];  Y  device bf16 [M, N], fully overwritten.
+ * Both factors are the fp32 sums of lowbit_gemm's arithmetic; the product is rounded to
+ * bf16 once.  Supports g = 64 or 128 (both bit widths); g = 32 returns LOWBIT_E_UNSUPPORTED.
+ * Runs on the large-M tile kernel for every M (small M computes correctly but at that
+ * kernel's speed).  Argument checks and errors as lowbit_gemm, with 2N weight rows.
+ */
+int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
+                       int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
+
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,

@@ -23,6 +23,10 @@ R4  Scale form: symmetric w = s * c for ternary too (the binary model card gives
     w = scale_g * b; no zero point is mentioned anywhere).
 R5  Invalid codes handed to the packer (ternary outside {-1,0,1}, binary outside
     {-1,1}) are packed as 0 bits and counted.
+R6  SwiGLU of the MLP-in linear (the MMDiT's 2 x 9216-output linear, mlx guide section
+    "组件架构"): its 2N output features are [gate | up], gate first, and the activation
+    is silu(gate) * up with silu(a) = a / (1 + exp(-a)).  Which half gates is not stated
+    on the pages.
 """
 from __future__ import annotations
 
@@ -167,6 +171,30 @@ def gemm_fsum_element(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
     c = np.asarray(codes)[n]
     s = np.asarray(scales, dtype=np.float16)[n].astype(np.float64)
     return math.fsum(float(x[k]) * int(c[k]) * float(s[k // g]) for k in range(c.shape[0]))
+
+
+def silu_f64(a: np.ndarray) -> np.ndarray:
+    """silu(a) = a * sigmoid(a) = a / (1 + exp(-a)) in fp64, evaluated as a * exp(a) / (1 + exp(a))
+    for negative a so that no exp overflows (reading R6)."""
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    pos = a >= 0
+    out[pos] = a[pos] / (1.0 + np.exp(-a[pos]))
+    e = np.exp(a[~pos])
+    out[~pos] = a[~pos] * e / (1.0 + e)
+    return out
+
+
+def swiglu_ref_f64(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, g: int) -> np.ndarray:
+    """Y[M, N] = silu(X @ Wg.T) * (X @ Wu.T) in fp64, where codes / scales hold 2N rows:
+    gate rows [0, N), then up rows [N, 2N) (reading R6).  Both factors are the exact
+    reference GEMM of the same rows."""
+    c = np.asarray(codes)
+    if c.shape[0] % 2:
+        raise ValueError("SwiGLU weights hold 2N rows (gate, then up)")
+    n = c.shape[0] // 2
+    y = gemm_ref_f64(x_bits, codes, scales, g)
+    return silu_f64(y[:, :n]) * y[:, n:]
 
 
 # ----------------------------------------------------------------------------------------

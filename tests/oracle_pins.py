@@ -36,7 +36,8 @@ def real_oracle():
     import oracle
     return SimpleNamespace(pack=oracle.pack, unpack=oracle.unpack, dequant_f64=oracle.dequant_f64,
                            gemm_ref_f64=oracle.gemm_ref_f64, gemm_fsum_element=oracle.gemm_fsum_element,
-                           bf16_bits_to_f64=oracle.bf16_bits_to_f64)
+                           bf16_bits_to_f64=oracle.bf16_bits_to_f64, silu_f64=oracle.silu_f64,
+                           swiglu_ref_f64=oracle.swiglu_ref_f64)
 
 
 # ----------------------------------------------------------------------------------------
@@ -191,3 +192,67 @@ def pin_binary_is_ternary_without_zeros(o, seed=8):
 
 ALL_PINS = [pin_golden_words, pin_bitstring, pin_unpack_unused_field, pin_group_blocks, pin_one_hot, pin_fsum,
             pin_statistics, pin_linearity, pin_library_matmul, pin_binary_is_ternary_without_zeros]
+
+
+# ----------------------------------------------------------------------------------------
+# SwiGLU (silu(gate) * up over the [gate | up] halves of the MLP-in weights)
+# ----------------------------------------------------------------------------------------
+
+# logistic function values sigma(t) = 1 / (1 + e^-t) and sigma(-t), to 16 significant digits
+_SIGMOID = {1.0: (0.7310585786300049, 0.2689414213699951), 2.0: (0.8807970779778823, 0.1192029220221176),
+            4.0: (0.9820137900379085, 0.01798620996209156), 20.0: (0.9999999979388463, 2.061153618190204e-09)}
+
+
+def pin_silu_values(o):
+    """silu(t) = t * sigma(t) and silu(-t) = -t * sigma(-t) at points where sigma is tabulated above."""
+    for t, (sp, sn) in _SIGMOID.items():
+        got = o.silu_f64(np.array([t, -t]))
+        assert abs(got[0] - t * sp) <= 1e-15 * t, (t, got[0])
+        assert abs(got[1] + t * sn) <= 1e-14 * t * sn, (t, got[1])
+    assert o.silu_f64(np.array([0.0]))[0] == 0.0
+
+
+def pin_silu_identities(o, seed=21):
+    """silu(-a) = silu(a) - a for all a; silu(a) -> a for large a; no overflow for very negative a."""
+    a = np.random.default_rng(seed).normal(0.0, 6.0, 4096)
+    lhs, rhs = o.silu_f64(-a), o.silu_f64(a) - a
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    big = o.silu_f64(np.array([50.0, 700.0]))
+    assert abs(big[0] - 50.0) <= 1e-12 and big[1] == 700.0
+    tiny = o.silu_f64(np.array([-800.0, -1e4]))
+    assert np.all(np.isfinite(tiny)) and np.all(tiny <= 0.0) and np.all(np.abs(tiny) < 1e-300)
+
+
+def pin_swiglu_fsum(o, seed=23):
+    """Each element equals silu(gate) * up with gate and up the correctly rounded sums of their exact
+    products (math.fsum) and silu from the math library's exp."""
+    M, N, K, g = 6, 32, 192, 64
+    x = gen_x(rng_for(seed, 11, 0), M, K)
+    c = gen_codes(rng_for(seed, 11, 1), 2 * N, K, 2)
+    sc = gen_scales(rng_for(seed, 11, 2), 2 * N, K, g)
+    y = o.swiglu_ref_f64(x, c, sc, g)
+    assert y.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            gt = o.gemm_fsum_element(x, c, sc, g, m, n)
+            up = o.gemm_fsum_element(x, c, sc, g, m, N + n)
+            want = gt / (1.0 + math.exp(-gt)) * up
+            assert abs(y[m, n] - want) <= 1e-12 * (abs(want) + 1e-30) + 1e-15, (m, n, y[m, n], want)
+
+
+def pin_swiglu_halves(o, seed=25):
+    """Gate rows first: the result is silu(Y of rows [0, N)) * (Y of rows [N, 2N)) of the plain
+    GEMM on each half alone, and swapping the halves changes it."""
+    M, N, K, g = 8, 48, 256, 64
+    x = gen_x(rng_for(seed, 12, 0), M, K)
+    c = gen_codes(rng_for(seed, 12, 1), 2 * N, K, 2)
+    sc = gen_scales(rng_for(seed, 12, 2), 2 * N, K, g)
+    gt = o.gemm_ref_f64(x, c[:N], sc[:N], g)
+    up = o.gemm_ref_f64(x, c[N:], sc[N:], g)
+    y = o.swiglu_ref_f64(x, c, sc, g)
+    assert np.allclose(y, gt / (1.0 + np.exp(-gt)) * up, rtol=1e-12, atol=1e-14)
+    swapped = o.swiglu_ref_f64(x, np.concatenate([c[N:], c[:N]]), np.concatenate([sc[N:], sc[:N]]), g)
+    assert not np.allclose(y, swapped, rtol=1e-3, atol=1e-3)
+
+
+SWIGLU_PINS = [pin_silu_values, pin_silu_identities, pin_swiglu_fsum, pin_swiglu_halves]

@@ -96,6 +96,21 @@ def test_gemm_rejects_before_touching_the_device():
     assert L.lowbit_gemm_batched(None, 0, None) == OK
 
 
+def test_swiglu_rejects_before_touching_the_device():
+    """lowbit_gemm_swiglu validates as lowbit_gemm with 2N weight rows, and takes g = 64 / 128 only."""
+    L = _lib.lib()
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, 250, 256, 64, 2, None) == INVALID      # N % 16
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, 256, 200, 64, 2, None) == INVALID      # K % g
+    assert L.lowbit_gemm_swiglu(0, A, A, A, 64, 256, 256, 64, 2, None) == INVALID      # null X
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, -16, 256, 64, 2, None) == INVALID
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, 256, 256, 32, 2, None) == UNSUPPORTED  # g = 32
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, 256, 256, 64, 3, None) == UNSUPPORTED  # bits
+    assert L.lowbit_gemm_swiglu(A + 8, A, A, A, 64, 256, 256, 64, 2, None) == ALIGN
+    # 2N rows of packed words: 2 x (2^19 rows x 4 KiB) = 4 GiB
+    assert L.lowbit_gemm_swiglu(A, A, A, A, 64, 1 << 19, 1 << 14, 64, 2, None) == UNSUPPORTED
+    assert L.lowbit_gemm_swiglu(0, 0, 0, 0, 0, 256, 256, 64, 2, None) == OK            # M == 0
+
+
 def test_variant_choice():
     """Tile choice: fewest rounds of tiles over 256 compute units, weighted by tile work.
     4608 x 3072 is 216 tiles of 256 x 256 (40 units idle) but exactly 256 of 288 x 192."""

@@ -10,9 +10,48 @@ from oracle import lowbit_ref as ref
 from tests import oracle_pins as P
 
 
-@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS, ids=lambda f: f.__name__)
 def test_pin_holds(pin):
     pin(P.real_oracle())
+
+
+def _swiglu_swapped(x, codes, scales, g):
+    n = codes.shape[0] // 2
+    y = oracle.gemm_ref_f64(x, codes, scales, g)
+    return oracle.silu_f64(y[:, n:]) * y[:, :n]
+
+
+def _swiglu_sigmoid(x, codes, scales, g):
+    n = codes.shape[0] // 2
+    y = oracle.gemm_ref_f64(x, codes, scales, g)
+    return 1.0 / (1.0 + np.exp(-y[:, :n])) * y[:, n:]
+
+
+def _silu_sign(a):
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(a))
+
+
+SWIGLU_PLANTED = {
+    "halves_swapped": dict(swiglu_ref_f64=_swiglu_swapped),
+    "sigmoid_not_silu": dict(swiglu_ref_f64=_swiglu_sigmoid),
+    "silu_sign_flipped": dict(silu_f64=_silu_sign,
+                              swiglu_ref_f64=lambda x, c, s, g: _silu_sign(
+                                  oracle.gemm_ref_f64(x, c, s, g)[:, :c.shape[0] // 2]) *
+                              oracle.gemm_ref_f64(x, c, s, g)[:, c.shape[0] // 2:]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWIGLU_PLANTED))
+def test_swiglu_planted_mistake_is_caught(name):
+    broken = SimpleNamespace(**{**vars(P.real_oracle()), **SWIGLU_PLANTED[name]})
+    failures = []
+    for pin in P.SWIGLU_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every SwiGLU pin"
 
 
 def test_statistics_binary():
