@@ -90,7 +90,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
-                    choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu"])
+                    choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu",
+                             "swiglu16"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -123,6 +124,9 @@ def problems_for(workload):
         # the MLP-in linear at 1024^2 (M = 4608, [gate | up] = 2 x 9216 weight rows, K = 3072) with
         # its SwiGLU fused: Y is [4608, 9216]
         return [W.Problem("m4608_mlp_in_swiglu", 4608, 18432, 3072, W.TERNARY, 64, 3, 2)]
+    if workload == "swiglu16":
+        # the same linear at M = 16 (the skinny denoise-step row count)
+        return [W.Problem("m16_mlp_in_swiglu", 16, 18432, 3072, W.TERNARY, 64, 3, 2)]
     raise ValueError(workload)
 
 
@@ -220,7 +224,7 @@ def main():
     probs = problems_for(a.workload)
     groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
     bufs = make_device_inputs(probs, a.seed)
-    swiglu = a.workload == "swiglu"
+    swiglu = a.workload in ("swiglu", "swiglu16")
     if swiglu:  # the fused SwiGLU writes half the columns
         x, w, s, _, g, bits = bufs[0]
         bufs[0] = (x, w, s, torch.empty((x.shape[0], w.shape[0] // 2), dtype=torch.bfloat16, device="cuda"), g, bits)
@@ -310,9 +314,10 @@ def main():
     variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
     traffic = measured_traffic(a.workload, variants)
 
-    if a.workload == "skinny":
-        metric, value, unit = "lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)", \
-            bytes_step / (elapsed / a.steps) / 1e9, "GB/s"
+    if a.workload in ("skinny", "swiglu16"):
+        metric = ("lowbit GEMM GB/s and % of HBM peak (M=16 denoise-step sweep, ternary g=64)" if a.workload == "skinny"
+                  else "lowbit fused SwiGLU GB/s and % of HBM peak (M=16 MLP-in, ternary g=64)")
+        value, unit = bytes_step / (elapsed / a.steps) / 1e9, "GB/s"
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:

@@ -75,7 +75,11 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* lds_wave_b
                                             0, 0);
 }
 
-template <int G, int LEN>
+// SWIGLU: the problem's W and S hold 2N rows (gate rows [0, N), up rows [N, 2N)) and Y[M, N] =
+// silu(X . Wgate^T) * (X . Wup^T).  A workgroup's CB (even) column blocks are then CB / 2 gate
+// blocks and the up blocks of the same output columns; after the K-slice reduction the up sums
+// reach the gate blocks' waves through LDS.  Whole K only (one split).
+template <int G, int LEN, bool SWIGLU = false>
 __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(ResidentArgs a) {
     constexpr int GPS = kStepCodes / G;  // scale groups per step: 4 or 2
     extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
@@ -93,8 +97,14 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     const int M = p.M, N = p.N, K = p.K;
     const int CB = a.cb, KS = a.ks, S = a.splits;
     const int cbi = wave % CB, ks = wave / CB;
-    const int cb = group * CB + cbi;
-    const bool active = cb < N / 16;  // wave-uniform
+    // global weight block of local block c (SwiGLU: gate block j or up block N/16 + j of output
+    // block j = group * CB/2 + c % (CB/2)), and whether it holds output columns
+    const int HB = CB / 2;
+    auto out_block = [&](int c) { return SWIGLU ? group * HB + c % HB : group * CB + c; };
+    auto w_block = [&](int c) { return SWIGLU && c >= HB ? N / 16 + out_block(c) : out_block(c); };
+    const int cb = w_block(cbi);
+    const bool active = out_block(cbi) < N / 16;  // wave-uniform
+    const int w_rows = SWIGLU ? 2 * N : N;
     const int T = K / kStepCodes;
     const int kb = split * T / S, tw = (split + 1) * T / S - kb;  // the workgroup's K range
     const int t_begin = ks * tw / KS;                             // relative to kb
@@ -122,9 +132,21 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     const uint32_t s_base = x_region_bytes(tw);
     const int dpr = int(s_row_lds(tw, G) / 4u);
     const int s_copies = (CB * 16 * dpr + 63) / 64;
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.S, uint32_t(N) * s_row);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.S, uint32_t(w_rows) * s_row);
     const uint32_t s_src = uint32_t(group * CB * 16) * s_row + uint32_t(kb * GPS) * 2u;
-    if (tw == T) {
+    if (SWIGLU) {
+        // row r of the region is row r % 16 of weight block w_block(r / 16); rows of blocks past
+        // the output read past the end of S (zeros, never used)
+        for (int j = wave; j < s_copies; j += nwaves) {
+            const int d = 64 * j + lane;
+            const int r = d / dpr, k = d - r * dpr;
+            const uint32_t src = r < CB * 16 && out_block(r / 16) < N / 16
+                                     ? uint32_t(w_block(r / 16) * 16 + (r & 15)) * s_row + uint32_t(kb * GPS) * 2u +
+                                           uint32_t(k) * 4u
+                                     : uint32_t(w_rows) * s_row;
+            dma4(sr, lds + s_base + 256 * j, src);
+        }
+    } else if (tw == T) {
         // whole K: the workgroup's rows of scales are one contiguous block of CB * 16 * s_row
         // bytes (a multiple of 16, at a multiple of 16); 16-byte copies, a quarter of the
         // instructions of the row-by-row 4-byte copies below (the region is rounded up to
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     // last column block, read through an empty resource: no memory traffic) ----
     const uint32_t w_row = uint32_t(K) / 4u;
     const uint32_t row = uint32_t(cb * 16 + n);
-    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, active ? uint32_t(N) * w_row : 0u);
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, active ? uint32_t(w_rows) * w_row : 0u);
     const __amdgpu_buffer_rsrc_t none = make_rsrc(p.W, 0u);
 #ifndef LOWBIT_RESIDENT_AHEAD
 #define LOWBIT_RESIDENT_AHEAD 2
@@ -238,6 +260,25 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
             }
         }
     }
+    if constexpr (SWIGLU) {
+        // up sums (blocks HB .. CB-1, slice 0) to the gate blocks' waves; silu(g) * u from the
+        // fp32 sums (the operand holds 2c: both halved), rounded to bf16 once
+        __syncthreads();  // the reduction's reads of the LDS are done
+        f32x4_t* xch = reinterpret_cast<f32x4_t*>(lds);
+        if (ks == 0 && cbi >= HB) xch[(cbi - HB) * 64 + lane] = acc;
+        __syncthreads();
+        if (ks == 0 && cbi < HB && active) {
+            const f32x4_t u = xch[cbi * 64 + lane];
+            const int col = out_block(cbi) * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 4 * q + e;
+                const float gt = 0.5f * acc[e];
+                if (m < M) p.Y[int64_t(m) * N + col] = float_to_bf16_bits(gt * (0.5f * u[e]) / (1.0f + __expf(-gt)));
+            }
+        }
+        return;
+    }
     const int col = cb * 16 + n;
     if (S == 1) {
         if (ks == 0 && active) {
@@ -303,32 +344,33 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, int LEN>
+template <int G, int LEN, bool SWIGLU = false>
 hipError_t launch_cfg(const ResidentArgs& a, uint32_t lds, hipStream_t stream) {
     // allow the dynamic LDS of the largest plan (once per kernel)
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN, SWIGLU>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kMaxLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_resident_kernel<G, LEN>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds, stream,
-                       a);
+    hipLaunchKernelGGL((gemm_resident_kernel<G, LEN, SWIGLU>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds,
+                       stream, a);
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool SWIGLU = false>
 hipError_t launch_g(const ResidentArgs& a, uint32_t lds, int len, hipStream_t stream) {
     switch (len) {
-        case 1: return launch_cfg<G, 1>(a, lds, stream);
-        case 2: return launch_cfg<G, 2>(a, lds, stream);
-        case 3: return launch_cfg<G, 3>(a, lds, stream);
-        case 4: return launch_cfg<G, 4>(a, lds, stream);
-        case 5: return launch_cfg<G, 5>(a, lds, stream);
-        case 6: return launch_cfg<G, 6>(a, lds, stream);
-        case 7: return launch_cfg<G, 7>(a, lds, stream);
-        case 8: return launch_cfg<G, 8>(a, lds, stream);
-        case 9: return launch_cfg<G, 9>(a, lds, stream);
-        case 10: return launch_cfg<G, 10>(a, lds, stream);
-        case 11: return launch_cfg<G, 11>(a, lds, stream);
-        case 12: return launch_cfg<G, 12>(a, lds, stream);
+        case 1: return launch_cfg<G, 1, SWIGLU>(a, lds, stream);
+        case 2: return launch_cfg<G, 2, SWIGLU>(a, lds, stream);
+        case 3: return launch_cfg<G, 3, SWIGLU>(a, lds, stream);
+        case 4: return launch_cfg<G, 4, SWIGLU>(a, lds, stream);
+        case 5: return launch_cfg<G, 5, SWIGLU>(a, lds, stream);
+        case 6: return launch_cfg<G, 6, SWIGLU>(a, lds, stream);
+        case 7: return launch_cfg<G, 7, SWIGLU>(a, lds, stream);
+        case 8: return launch_cfg<G, 8, SWIGLU>(a, lds, stream);
+        case 9: return launch_cfg<G, 9, SWIGLU>(a, lds, stream);
+        case 10: return launch_cfg<G, 10, SWIGLU>(a, lds, stream);
+        case 11: return launch_cfg<G, 11, SWIGLU>(a, lds, stream);
+        case 12: return launch_cfg<G, 12, SWIGLU>(a, lds, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -471,6 +513,35 @@ hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g
     const uint32_t red = uint32_t(pl.cb * pl.ks) * 1024u;  // the K-slice reduction reuses the LDS
     lds = lds > red ? lds : red;
     return g == 64 ? launch_g<64>(a, lds, pl.len, stream) : launch_g<128>(a, lds, pl.len, stream);
+}
+
+// Fused SwiGLU (gate rows [0, N), up rows [N, 2N) of W and S; Y is [M, N]): a whole-K plan whose
+// workgroups hold an even number of column blocks -- half gate, half the up blocks of the same
+// output columns -- enough that the pairs fill one round over the compute units.  Returns
+// hipErrorNotSupported where no such plan fits (the caller then takes the tile kernel).
+hipError_t launch_gemm_resident_swiglu(const GemmProblem& p, int g, hipStream_t stream) {
+    if (!resident_supported(p.M, 2 * int64_t(p.N), p.K, g, 2)) return hipErrorNotSupported;
+    const int T = p.K / kStepCodes;
+    const int64_t out_blocks = p.N / 16;
+    int cb = int((2 * out_blocks + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    cb = cb < 2 ? 2 : cb + (cb & 1);
+    if (cb > kMaxWaves) return hipErrorNotSupported;
+    int ks = kMaxWaves / cb;
+    ks = ks < T ? ks : T;
+    const int len = (T + ks - 1) / ks;
+    if (len > kMaxLen || lds_bytes(T, g, cb) > uint32_t(kMaxLds)) return hipErrorNotSupported;
+    ResidentArgs a{};
+    a.grp.p[0] = p;
+    a.grp.count = 1;
+    a.tiles = int((out_blocks + cb / 2 - 1) / (cb / 2));
+    a.grp.tile_end[0] = a.tiles;
+    a.cb = cb;
+    a.ks = ks;
+    a.splits = 1;
+    uint32_t lds = lds_bytes(T, g, cb);
+    const uint32_t red = uint32_t(cb * ks) * 1024u;  // the K-slice reduction reuses the LDS
+    lds = lds > red ? lds : red;
+    return g == 64 ? launch_g<64, true>(a, lds, len, stream) : launch_g<128, true>(a, lds, len, stream);
 }
 
 }  // namespace lowbit

@@ -273,7 +273,10 @@ int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
         hipLaunchKernelGGL(zero_fill_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p.Y, n);
         e = hipGetLastError();
     } else {
-        e = lowbit::launch_gemm_tile16_swiglu(&p, 1, g, bits, s);
+        // skinny ternary M on the resident kernel where a whole-K plan fits, else the tile kernel
+        e = hipErrorNotSupported;
+        if (bits == 2 && M <= 16) e = lowbit::launch_gemm_resident_swiglu(p, g, s);
+        if (e == hipErrorNotSupported) e = lowbit::launch_gemm_tile16_swiglu(&p, 1, g, bits, s);
     }
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }

@@ -64,6 +64,8 @@ size_t resident_workspace_bytes(const ResidentPlan& plan);
 bool resident_preferred(const GemmProblem* probs, int count, int g, bool may_split);
 hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g, const ResidentPlan& plan,
                                       void* workspace, hipStream_t stream);
+// Fused SwiGLU on the resident kernel (whole K); hipErrorNotSupported where no plan applies.
+hipError_t launch_gemm_resident_swiglu(const GemmProblem& p, int g, hipStream_t stream);
 
 // Grouped launch: problems of one (g, bits) class; one launch per kernel family and per
 // kMaxGroup problems.

@@ -50,7 +50,10 @@ def _check(y_bits, inp, g, what, cols=None):
         got = y_bits[:, cols]
     r = oracle.check_tolerance(got, ref)
     assert r["ok"], f"{what}: {r}"
-    assert r["rel_frob"] <= REL_ALARM, f"{what}: rel_frob {r['rel_frob']}"
+    # logic-error alarm: well above the bf16 output rounding floor, which for a few outputs can
+    # itself exceed REL_ALARM (16 outputs: 2.5e-3 measured)
+    floor = oracle.check_tolerance(oracle.f64_to_bf16_bits_rne(ref), ref)["rel_frob"]
+    assert r["rel_frob"] <= max(REL_ALARM, 1.5 * floor), f"{what}: rel_frob {r['rel_frob']} (floor {floor})"
 
 
 # (M, N, K, g, bits): several M and N tiles with ragged edges (N % 96 != 0 leaves a partly
@@ -65,6 +68,20 @@ def test_swiglu_parity(M, N, K, g, bits):
     inp = _inputs(M, N, K, g, bits)
     y, _ = _run(inp, g, bits)
     _check(y, inp, g, f"swiglu {M}x{N}x{K} g{g} b{bits}")
+
+
+# skinny M (ternary, K % 256 == 0): the resident kernel's SwiGLU mode where a whole-K plan fits
+# (workgroups of gate blocks and the matching up blocks), the tile kernel otherwise (K = 12288
+# at M = 16 does not fit one workgroup's LDS)
+SKINNY = [(16, 9216, 3072, 64), (5, 400, 1280, 128), (16, 1008, 4352, 64), (1, 16, 256, 64), (16, 3072, 12288, 64),
+          (11, 3072, 9216, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", SKINNY)
+def test_swiglu_skinny_parity(M, N, K, g):
+    inp = _inputs(M, N, K, g, 2, seed=7)
+    y, _ = _run(inp, g, 2)
+    _check(y, inp, g, f"swiglu skinny {M}x{N}x{K} g{g}")
 
 
 def test_swiglu_mlp_in_full_size_sampled():
