@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
                     choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu",
-                             "swiglu16"])
+                             "swiglu16", "residual"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -124,6 +124,9 @@ def problems_for(workload):
         # the MLP-in linear at 1024^2 (M = 4608, [gate | up] = 2 x 9216 weight rows, K = 3072) with
         # its SwiGLU fused: Y is [4608, 9216]
         return [W.Problem("m4608_mlp_in_swiglu", 4608, 18432, 3072, W.TERNARY, 64, 3, 2)]
+    if workload == "residual":
+        # the MLP-out linear at 1024^2 (M = 4608, 9216 -> 3072) with its gated residual update fused
+        return [W.Problem("m4608_mlp_out_residual", 4608, 3072, 9216, W.TERNARY, 64, 3, 3)]
     if workload == "swiglu16":
         # the same linear at M = 16 (the skinny denoise-step row count)
         return [W.Problem("m16_mlp_in_swiglu", 16, 18432, 3072, W.TERNARY, 64, 3, 2)]
@@ -133,6 +136,11 @@ def problems_for(workload):
 def swiglu_bytes(p):
     """Algorithmic bytes of a fused SwiGLU problem: Y has half the columns of the weight rows."""
     return p.bytes_moved() - p.M * (p.N // 2) * 2
+
+
+def residual_bytes(p):
+    """Algorithmic bytes of a fused gated-residual problem: the GEMM's, plus R read and the gate."""
+    return p.bytes_moved() + p.M * p.N * 2 + p.N * 2
 
 
 def make_device_inputs(probs, seed):
@@ -225,6 +233,13 @@ def main():
     groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
     bufs = make_device_inputs(probs, a.seed)
     swiglu = a.workload in ("swiglu", "swiglu16")
+    residual = a.workload == "residual"
+    if residual:  # residual stream R (N(0,1)) and a per-feature gate, drawn once
+        x0, w0 = bufs[0][0], bufs[0][1]
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(a.seed + 77)
+        res_r = torch.randn((x0.shape[0], w0.shape[0]), generator=gen, device="cuda").to(torch.bfloat16)
+        res_g = torch.randn((w0.shape[0],), generator=gen, device="cuda").to(torch.bfloat16)
     if swiglu:  # the fused SwiGLU writes half the columns
         x, w, s, _, g, bits = bufs[0]
         bufs[0] = (x, w, s, torch.empty((x.shape[0], w.shape[0] // 2), dtype=torch.bfloat16, device="cuda"), g, bits)
@@ -244,6 +259,9 @@ def main():
         if swiglu:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm_swiglu(x, w, s, g, bits, out=y)
+        elif residual:
+            x, w, s, y, g, bits = bufs[grp[0]]
+            lb.gemm_residual(x, w, s, g, bits, res_r, res_g, out=y)
         elif len(grp) == 1:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm(x, w, s, g, bits, out=y, workspace=ws)
@@ -302,7 +320,7 @@ def main():
                for i in range(len(groups))]
 
     flops_step = sum(p.flops for p in probs)
-    bytes_step = sum(swiglu_bytes(p) if swiglu else p.bytes_moved() for p in probs)
+    bytes_step = sum(swiglu_bytes(p) if swiglu else residual_bytes(p) if residual else p.bytes_moved() for p in probs)
     ms_per_step = elapsed * 1e3 / a.steps
     tflops = flops_step / (elapsed / a.steps) / 1e12
     launches = len(groups)

@@ -169,6 +169,37 @@ def gemm_swiglu(x, words, scales, g: int, bits: int, out=None):
     return out
 
 
+def gemm_residual(x, words, scales, g: int, bits: int, residual, gate, out=None):
+    """Y[M, N] = residual + gate[n] * (X . dequant(W)^T) in bf16 (lowbit_gemm_residual).
+    `out` may be `residual` itself (in-place update of the residual stream)."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    _require(words, torch.int32, "words")
+    _require(scales, torch.float16, "scales")
+    _require(residual, torch.bfloat16, "residual")
+    _require(gate, torch.bfloat16, "gate", ndim=1)
+    M, K = x.shape
+    N = words.shape[0]
+    if words.shape[1] != words_per_row(K, bits):
+        raise ValueError(f"words must be [N, K*bits/32] = [{N}, {words_per_row(K, bits)}], got {tuple(words.shape)}")
+    if K % g or tuple(scales.shape) != (N, K // g):
+        raise ValueError(f"scales must be [N, K/g] = [{N}, {K // g if g else 0}], got {tuple(scales.shape)}")
+    if tuple(residual.shape) != (M, N) or tuple(gate.shape) != (N,):
+        raise ValueError("residual must be [M, N] and gate [N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().lowbit_gemm_residual(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                                    ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(residual.data_ptr()),
+                                    ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                    M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
+    _check(st, "lowbit_gemm_residual")
+    return out
+
+
 def _problem_array(problems):
     torch = _torch()
     if len(problems) > MAX_BATCH:

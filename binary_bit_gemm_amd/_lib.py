@@ -16,6 +16,7 @@ SIGNATURES = {
     "lowbit_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "lowbit_gemm_batched": (_INT, [_VP, _INT, _VP]),
     "lowbit_gemm_swiglu": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "lowbit_gemm_residual": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "lowbit_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _INT, _INT]),
     "lowbit_gemm_ex": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP, ctypes.c_size_t, _VP]),
     "lowbit_batched_workspace_size": (ctypes.c_size_t, [_VP, _INT]),

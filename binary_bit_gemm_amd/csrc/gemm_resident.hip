@@ -75,12 +75,14 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* lds_wave_b
                                             0, 0);
 }
 
-// SWIGLU: the problem's W and S hold 2N rows (gate rows [0, N), up rows [N, 2N)) and Y[M, N] =
-// silu(X . Wgate^T) * (X . Wup^T).  A workgroup's CB (even) column blocks are then CB / 2 gate
-// blocks and the up blocks of the same output columns; after the K-slice reduction the up sums
-// reach the gate blocks' waves through LDS.  Whole K only (one split).
-template <int G, int LEN, bool SWIGLU = false>
+// EPI = kEpiSwiglu: the problem's W and S hold 2N rows (gate rows [0, N), up rows [N, 2N)) and
+// Y[M, N] = silu(X . Wgate^T) * (X . Wup^T).  A workgroup's CB (even) column blocks are then CB / 2
+// gate blocks and the up blocks of the same output columns; after the K-slice reduction the up
+// sums reach the gate blocks' waves through LDS.  EPI = kEpiResidual: Y = R + gate[n] * (X . W^T)
+// (Y may be R: each element is read and written by the same lane).  Both: whole K only (one split).
+template <int G, int LEN, int EPI = kEpiPlain>
 __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(ResidentArgs a) {
+    constexpr bool SWIGLU = EPI == kEpiSwiglu;
     constexpr int GPS = kStepCodes / G;  // scale groups per step: 4 or 2
     extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
@@ -282,10 +284,16 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     const int col = cb * 16 + n;
     if (S == 1) {
         if (ks == 0 && active) {
+            const float gt = EPI == kEpiResidual ? static_cast<float>(__builtin_bit_cast(__bf16, p.gate[col])) : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = 4 * q + e;
-                if (m < M) p.Y[int64_t(m) * N + col] = float_to_bf16_bits(0.5f * acc[e]);  // operand holds 2c
+                if (m < M) {
+                    float v = 0.5f * acc[e];  // operand holds 2c
+                    if constexpr (EPI == kEpiResidual)
+                        v = __builtin_fmaf(gt, v, static_cast<float>(__builtin_bit_cast(__bf16, p.R[int64_t(m) * N + col])));
+                    p.Y[int64_t(m) * N + col] = float_to_bf16_bits(v);
+                }
             }
         }
         return;
@@ -344,33 +352,33 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, int LEN, bool SWIGLU = false>
+template <int G, int LEN, int EPI = kEpiPlain>
 hipError_t launch_cfg(const ResidentArgs& a, uint32_t lds, hipStream_t stream) {
     // allow the dynamic LDS of the largest plan (once per kernel)
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN, SWIGLU>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN, EPI>), hipFuncAttributeMaxDynamicSharedMemorySize,
         kMaxLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_resident_kernel<G, LEN, SWIGLU>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds,
+    hipLaunchKernelGGL((gemm_resident_kernel<G, LEN, EPI>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds,
                        stream, a);
     return hipGetLastError();
 }
 
-template <int G, bool SWIGLU = false>
+template <int G, int EPI = kEpiPlain>
 hipError_t launch_g(const ResidentArgs& a, uint32_t lds, int len, hipStream_t stream) {
     switch (len) {
-        case 1: return launch_cfg<G, 1, SWIGLU>(a, lds, stream);
-        case 2: return launch_cfg<G, 2, SWIGLU>(a, lds, stream);
-        case 3: return launch_cfg<G, 3, SWIGLU>(a, lds, stream);
-        case 4: return launch_cfg<G, 4, SWIGLU>(a, lds, stream);
-        case 5: return launch_cfg<G, 5, SWIGLU>(a, lds, stream);
-        case 6: return launch_cfg<G, 6, SWIGLU>(a, lds, stream);
-        case 7: return launch_cfg<G, 7, SWIGLU>(a, lds, stream);
-        case 8: return launch_cfg<G, 8, SWIGLU>(a, lds, stream);
-        case 9: return launch_cfg<G, 9, SWIGLU>(a, lds, stream);
-        case 10: return launch_cfg<G, 10, SWIGLU>(a, lds, stream);
-        case 11: return launch_cfg<G, 11, SWIGLU>(a, lds, stream);
-        case 12: return launch_cfg<G, 12, SWIGLU>(a, lds, stream);
+        case 1: return launch_cfg<G, 1, EPI>(a, lds, stream);
+        case 2: return launch_cfg<G, 2, EPI>(a, lds, stream);
+        case 3: return launch_cfg<G, 3, EPI>(a, lds, stream);
+        case 4: return launch_cfg<G, 4, EPI>(a, lds, stream);
+        case 5: return launch_cfg<G, 5, EPI>(a, lds, stream);
+        case 6: return launch_cfg<G, 6, EPI>(a, lds, stream);
+        case 7: return launch_cfg<G, 7, EPI>(a, lds, stream);
+        case 8: return launch_cfg<G, 8, EPI>(a, lds, stream);
+        case 9: return launch_cfg<G, 9, EPI>(a, lds, stream);
+        case 10: return launch_cfg<G, 10, EPI>(a, lds, stream);
+        case 11: return launch_cfg<G, 11, EPI>(a, lds, stream);
+        case 12: return launch_cfg<G, 12, EPI>(a, lds, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -515,25 +523,31 @@ hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g
     return g == 64 ? launch_g<64>(a, lds, pl.len, stream) : launch_g<128>(a, lds, pl.len, stream);
 }
 
-// Fused SwiGLU (gate rows [0, N), up rows [N, 2N) of W and S; Y is [M, N]): a whole-K plan whose
+// Fused epilogues, whole K only; hipErrorNotSupported where no plan fits (the caller then takes
+// the tile kernel).  SwiGLU (gate rows [0, N), up rows [N, 2N) of W and S; Y is [M, N]): the
 // workgroups hold an even number of column blocks -- half gate, half the up blocks of the same
-// output columns -- enough that the pairs fill one round over the compute units.  Returns
-// hipErrorNotSupported where no such plan fits (the caller then takes the tile kernel).
-hipError_t launch_gemm_resident_swiglu(const GemmProblem& p, int g, hipStream_t stream) {
-    if (!resident_supported(p.M, 2 * int64_t(p.N), p.K, g, 2)) return hipErrorNotSupported;
+// output columns -- enough that the pairs fill one round over the compute units.  Residual: the
+// plain whole-K plan.
+hipError_t launch_gemm_resident_epilogue(const GemmProblem& p, int g, int epi, hipStream_t stream) {
+    const bool swiglu = epi == kEpiSwiglu;
+    const int64_t w_rows = swiglu ? 2 * int64_t(p.N) : p.N;
+    if (!resident_supported(p.M, w_rows, p.K, g, 2) || (epi != kEpiSwiglu && epi != kEpiResidual))
+        return hipErrorNotSupported;
     const int T = p.K / kStepCodes;
     const int64_t out_blocks = p.N / 16;
-    int cb = int((2 * out_blocks + kTargetWorkgroups - 1) / kTargetWorkgroups);
-    cb = cb < 2 ? 2 : cb + (cb & 1);
+    int cb = int((w_rows / 16 + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    cb = cb < 1 ? 1 : cb;
+    if (swiglu) cb = cb < 2 ? 2 : cb + (cb & 1);
     if (cb > kMaxWaves) return hipErrorNotSupported;
     int ks = kMaxWaves / cb;
     ks = ks < T ? ks : T;
     const int len = (T + ks - 1) / ks;
     if (len > kMaxLen || lds_bytes(T, g, cb) > uint32_t(kMaxLds)) return hipErrorNotSupported;
+    const int per_tile = swiglu ? cb / 2 : cb;  // output column blocks per workgroup
     ResidentArgs a{};
     a.grp.p[0] = p;
     a.grp.count = 1;
-    a.tiles = int((out_blocks + cb / 2 - 1) / (cb / 2));
+    a.tiles = int((out_blocks + per_tile - 1) / per_tile);
     a.grp.tile_end[0] = a.tiles;
     a.cb = cb;
     a.ks = ks;
@@ -541,7 +555,8 @@ hipError_t launch_gemm_resident_swiglu(const GemmProblem& p, int g, hipStream_t 
     uint32_t lds = lds_bytes(T, g, cb);
     const uint32_t red = uint32_t(cb * ks) * 1024u;  // the K-slice reduction reuses the LDS
     lds = lds > red ? lds : red;
-    return g == 64 ? launch_g<64, true>(a, lds, len, stream) : launch_g<128, true>(a, lds, len, stream);
+    if (swiglu) return g == 64 ? launch_g<64, kEpiSwiglu>(a, lds, len, stream) : launch_g<128, kEpiSwiglu>(a, lds, len, stream);
+    return g == 64 ? launch_g<64, kEpiResidual>(a, lds, len, stream) : launch_g<128, kEpiResidual>(a, lds, len, stream);
 }
 
 }  // namespace lowbit

@@ -69,12 +69,15 @@ struct Cfg16 {
     static_assert(BITS == 1 || BITS == 2, "binary or ternary codes");
 };
 
-// SWIGLU: the problem's W and S hold 2N rows, gate rows [0, N) then up rows [N, 2N), and Y[M, N] =
-// silu(X . Wgate^T) * (X . Wup^T), both factors taken from the fp32 sums and rounded to bf16 once.
-// A wave's two 16-column blocks are then the gate and the up rows of the same 16 output columns,
-// so the epilogue combines them in registers; a BN-row weight tile makes BN / 2 output columns.
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, bool SWIGLU = false>
+// EPI = kEpiSwiglu: the problem's W and S hold 2N rows, gate rows [0, N) then up rows [N, 2N), and
+// Y[M, N] = silu(X . Wgate^T) * (X . Wup^T), both factors taken from the fp32 sums and rounded to
+// bf16 once.  A wave's two 16-column blocks are then the gate and the up rows of the same 16
+// output columns, so the epilogue combines them in registers; a BN-row weight tile makes BN / 2
+// output columns.  EPI = kEpiResidual: Y = R + gate[n] * (X . W^T) in fp32, rounded once (Y may
+// be R: every element is read and written by the same lane).
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int EPI = kEpiPlain>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp) {
+    constexpr bool SWIGLU = EPI == kEpiSwiglu;
     using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
     constexpr int kWSpb = C::W_SPB;
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && C::WAVES == 4), "K groups of 4 waves, two of them");
@@ -412,8 +415,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         return uint32_t(float_to_bf16_bits(lo)) | (uint32_t(float_to_bf16_bits(hi)) << 16);
     };
     // one 16x16 block of fp32 results to bf16 at columns nblk .. nblk + 15 of row block mb
-    auto store_block = [&](const f32x4_t& a, int nblk, int mb) {
+    auto store_block = [&](f32x4_t a, int nblk, int mb) {
         if (nblk >= N) return;  // N % 16 == 0: a block is in or out as a whole
+        if constexpr (EPI == kEpiResidual) {
+            // lane (q, l16) holds column nblk + l16 of rows 4q + i: the gated residual update
+            const int col = nblk + l16;
+            const float gt = static_cast<float>(__builtin_bit_cast(__bf16, p.gate[col]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm0 + mb * 16 + 4 * q + i;
+                const float r = m < M ? static_cast<float>(__builtin_bit_cast(__bf16, p.R[int64_t(m) * N + col])) : 0.f;
+                a[i] = __builtin_fmaf(gt, a[i], r);
+            }
+        }
         const uint32_t P = pack(a[0], a[1]);  // rows 0, 1 of column b4
         const uint32_t Q = pack(a[2], a[3]);  // rows 2, 3
         const uint32_t own = lower_pair ? P : Q;
@@ -447,18 +461,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     }
 }
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, bool SWIGLU = false>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, int EPI = kEpiPlain>
 hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
     ProblemGroup grp{};
     int total = 0;
-    constexpr int kOutBn = SWIGLU ? BN / 2 : BN;
+    constexpr int kOutBn = EPI == kEpiSwiglu ? BN / 2 : BN;
     for (int i = 0; i < count; ++i) {
         grp.p[i] = probs[i];
         total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + kOutBn - 1) / kOutBn);
         grp.tile_end[i] = total;
     }
     grp.count = count;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, SWIGLU>), dim3(total),
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI>), dim3(total),
                        dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
     return hipGetLastError();
 }
@@ -486,15 +500,24 @@ hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hi
     return launch_cfg16<G, BITS, 288, 192, 2, 6>(probs, count, stream);
 }
 
-template <int G, int BITS>
-hipError_t launch_swiglu16(const GemmProblem* probs, int count, hipStream_t stream) {
-    return launch_cfg16<G, BITS, 288, 192, 2, 6, 1, true>(probs, count, stream);
+template <int G, int BITS, int EPI>
+hipError_t launch_epi16(const GemmProblem* probs, int count, hipStream_t stream) {
+    return launch_cfg16<G, BITS, 288, 192, 2, 6, 1, EPI>(probs, count, stream);
 }
 
-hipError_t launch_gemm_tile16_swiglu(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
+template <int EPI>
+hipError_t launch_epi16_gb(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
+    if (bits == 2)
+        return g == 64 ? launch_epi16<64, 2, EPI>(probs, count, stream) : launch_epi16<128, 2, EPI>(probs, count, stream);
+    return g == 64 ? launch_epi16<64, 1, EPI>(probs, count, stream) : launch_epi16<128, 1, EPI>(probs, count, stream);
+}
+
+hipError_t launch_gemm_tile16_epilogue(const GemmProblem* probs, int count, int g, int bits, int epi,
+                                       hipStream_t stream) {
     if (count < 1 || count > kMaxGroup || !tile16_supported(g, bits)) return hipErrorInvalidValue;
-    if (bits == 2) return g == 64 ? launch_swiglu16<64, 2>(probs, count, stream) : launch_swiglu16<128, 2>(probs, count, stream);
-    return g == 64 ? launch_swiglu16<64, 1>(probs, count, stream) : launch_swiglu16<128, 1>(probs, count, stream);
+    if (epi == kEpiSwiglu) return launch_epi16_gb<kEpiSwiglu>(probs, count, g, bits, stream);
+    if (epi == kEpiResidual) return launch_epi16_gb<kEpiResidual>(probs, count, g, bits, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,

@@ -275,8 +275,33 @@ int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
     } else {
         // skinny ternary M on the resident kernel where a whole-K plan fits, else the tile kernel
         e = hipErrorNotSupported;
-        if (bits == 2 && M <= 16) e = lowbit::launch_gemm_resident_swiglu(p, g, s);
-        if (e == hipErrorNotSupported) e = lowbit::launch_gemm_tile16_swiglu(&p, 1, g, bits, s);
+        if (bits == 2 && M <= 16) e = lowbit::launch_gemm_resident_epilogue(p, g, lowbit::kEpiSwiglu, s);
+        if (e == hipErrorNotSupported) e = lowbit::launch_gemm_tile16_epilogue(&p, 1, g, bits, lowbit::kEpiSwiglu, s);
+    }
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
+int lowbit_gemm_residual(const void* X, const uint32_t* W, const void* S, const void* R, const void* gate, void* Y,
+                         int64_t M, int64_t N, int64_t K, int g, int bits, void* stream) {
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    if (R == nullptr || gate == nullptr) return LOWBIT_E_INVALID;
+    if (!aligned16(R) || !aligned16(gate)) return LOWBIT_E_ALIGN;
+    if (!lowbit::tile16_supported(g, bits)) return LOWBIT_E_UNSUPPORTED;
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (K == 0) {  // Y = R + gate * 0
+        e = R == Y ? hipSuccess
+                   : hipMemcpyAsync(Y, R, size_t(M) * size_t(N) * 2u, hipMemcpyDeviceToDevice, s);
+    } else {
+        lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                              static_cast<uint16_t*>(Y), int(M), int(N), int(K),
+                              static_cast<const uint16_t*>(R), static_cast<const uint16_t*>(gate)};
+        e = hipErrorNotSupported;
+        if (bits == 2 && M <= 16) e = lowbit::launch_gemm_resident_epilogue(p, g, lowbit::kEpiResidual, s);
+        if (e == hipErrorNotSupported) e = lowbit::launch_gemm_tile16_epilogue(&p, 1, g, bits, lowbit::kEpiResidual, s);
     }
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }

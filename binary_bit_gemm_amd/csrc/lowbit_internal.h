@@ -13,7 +13,14 @@ struct GemmProblem {
     const uint16_t* S;  // fp16 [N, K/g]
     uint16_t* Y;        // bf16 [M, N]
     int M, N, K;
+    const uint16_t* R = nullptr;     // gated-residual epilogue only: bf16 residual [M, N] (may be Y)
+    const uint16_t* gate = nullptr;  // gated-residual epilogue only: bf16 gate [N]
 };
+
+// Epilogues of the 16x16-block tile kernel and of the resident kernel.
+constexpr int kEpiPlain = 0;     // Y = X . W^T
+constexpr int kEpiSwiglu = 1;    // W holds [gate | up] rows: Y = silu(X . Wg^T) * (X . Wu^T)
+constexpr int kEpiResidual = 2;  // Y = R + gate[n] * (X . W^T)
 
 // Several independent problems of one (g, bits) class in one launch.  Workgroup w of the
 // launch belongs to the first problem i with w < tile_end[i] (inclusive prefix sums of the
@@ -64,8 +71,8 @@ size_t resident_workspace_bytes(const ResidentPlan& plan);
 bool resident_preferred(const GemmProblem* probs, int count, int g, bool may_split);
 hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g, const ResidentPlan& plan,
                                       void* workspace, hipStream_t stream);
-// Fused SwiGLU on the resident kernel (whole K); hipErrorNotSupported where no plan applies.
-hipError_t launch_gemm_resident_swiglu(const GemmProblem& p, int g, hipStream_t stream);
+// Fused epilogues on the resident kernel (whole K); hipErrorNotSupported where no plan applies.
+hipError_t launch_gemm_resident_epilogue(const GemmProblem& p, int g, int epi, hipStream_t stream);
 
 // Grouped launch: problems of one (g, bits) class; one launch per kernel family and per
 // kMaxGroup problems.
@@ -81,9 +88,11 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits);
 int pick_tile_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
 const char* tile_variant_name(int variant);
 bool tile16_supported(int g, int bits);
-// Fused SwiGLU on the 288 x 192 16x16-block tile: each problem's W and S hold 2N rows (gate
-// rows [0, N), up rows [N, 2N)), Y is [M, N].
-hipError_t launch_gemm_tile16_swiglu(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream);
+// Fused epilogues on the 288 x 192 16x16-block tile (epi = kEpiSwiglu: each problem's W and S
+// hold 2N rows, gate rows [0, N) then up rows [N, 2N), Y is [M, N]; epi = kEpiResidual: the
+// problem's R and gate are set).
+hipError_t launch_gemm_tile16_epilogue(const GemmProblem* probs, int count, int g, int bits, int epi,
+                                       hipStream_t stream);
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                     hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);

@@ -168,6 +168,23 @@ int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* work
 int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
                        int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
 
+/*
+ * lowbit_gemm_residual -- a block's output linear with its gated residual update fused:
+ *   Y[m, n] = R[m, n] + gate[n] * (X . dequant(W)^T)[m, n]
+ * (the modulation gate of an MMDiT block applied to the proj / MLP-out linear, added to the
+ * residual stream; the mlx page's component architecture names the modulated blocks, the exact
+ * form is this library's reading).
+ *   X, W, S, M, N, K, g, bits  as lowbit_gemm;
+ *   R     device bf16 [M, N], the residual; may be the same memory as Y (in-place update);
+ *   gate  device bf16 [N], one factor per output feature;
+ *   Y     device bf16 [M, N], fully overwritten.
+ * The product, the gate multiply and the add are done in fp32 and rounded to bf16 once.
+ * g = 64 or 128 (g = 32 returns LOWBIT_E_UNSUPPORTED); a null R or gate returns
+ * LOWBIT_E_INVALID, an unaligned one LOWBIT_E_ALIGN.  K = 0 gives Y = R.
+ */
+int lowbit_gemm_residual(const void* X, const uint32_t* W, const void* S, const void* R, const void* gate,
+                         void* Y, int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
+
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,

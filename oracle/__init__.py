@@ -30,6 +30,6 @@ from .lowbit_ref import (  # noqa: F401
     TERNARY, BINARY,
     bf16_bits_to_f64, f64_to_bf16_bits_rne,
     pack, unpack, dequant_f64, gemm_ref_f64, gemm_ref_from_words, gemm_fsum_element,
-    silu_f64, swiglu_ref_f64,
+    silu_f64, swiglu_ref_f64, residual_ref_f64,
     check_tolerance, REL_FROB_TOL, ELEM_TOL,
 )

@@ -27,6 +27,9 @@ R6  SwiGLU of the MLP-in linear (the MMDiT's 2 x 9216-output linear, mlx guide s
     "组件架构"): its 2N output features are [gate | up], gate first, and the activation
     is silu(gate) * up with silu(a) = a / (1 + exp(-a)).  Which half gates is not stated
     on the pages.
+R7  Gated residual of a block's output linear (the mlx guide's modulated MMDiT blocks,
+    section "组件架构"): Y = R + gate[n] * (X . W^T)[m, n] with a per-feature gate; the exact
+    form is a reading.
 """
 from __future__ import annotations
 
@@ -195,6 +198,18 @@ def swiglu_ref_f64(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, g:
     n = c.shape[0] // 2
     y = gemm_ref_f64(x_bits, codes, scales, g)
     return silu_f64(y[:, :n]) * y[:, n:]
+
+
+def residual_ref_f64(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, g: int,
+                     r_bits: np.ndarray, gate_bits: np.ndarray) -> np.ndarray:
+    """Y[m, n] = R[m, n] + gate[n] * (X @ W.T)[m, n] in fp64, R and gate given as bf16 bit
+    patterns (reading R7)."""
+    y = gemm_ref_f64(x_bits, codes, scales, g)
+    r = bf16_bits_to_f64(r_bits)
+    gt = bf16_bits_to_f64(gate_bits)
+    if r.shape != y.shape or gt.shape != (y.shape[1],):
+        raise ValueError("residual must be [M, N] and gate [N]")
+    return r + gt[None, :] * y
 
 
 # ----------------------------------------------------------------------------------------

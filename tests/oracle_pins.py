@@ -37,7 +37,7 @@ def real_oracle():
     return SimpleNamespace(pack=oracle.pack, unpack=oracle.unpack, dequant_f64=oracle.dequant_f64,
                            gemm_ref_f64=oracle.gemm_ref_f64, gemm_fsum_element=oracle.gemm_fsum_element,
                            bf16_bits_to_f64=oracle.bf16_bits_to_f64, silu_f64=oracle.silu_f64,
-                           swiglu_ref_f64=oracle.swiglu_ref_f64)
+                           swiglu_ref_f64=oracle.swiglu_ref_f64, residual_ref_f64=oracle.residual_ref_f64)
 
 
 # ----------------------------------------------------------------------------------------
@@ -256,3 +256,74 @@ def pin_swiglu_halves(o, seed=25):
 
 
 SWIGLU_PINS = [pin_silu_values, pin_silu_identities, pin_swiglu_fsum, pin_swiglu_halves]
+
+
+# ----------------------------------------------------------------------------------------
+# Gated residual (Y = R + gate[n] * (X . W^T))
+# ----------------------------------------------------------------------------------------
+
+def _bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Exact bf16 bit patterns of values that bf16 holds exactly (the top half of their fp32 bits)."""
+    f = np.asarray(v, dtype=np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64)), "not exact in fp32"
+    b = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << np.uint32(16)).view(np.float32), f), "not exact in bf16"
+    return b
+
+
+def _residual_case(seed, M=6, N=32, K=192, g=64):
+    x = gen_x(rng_for(seed, 13, 0), M, K)
+    c = gen_codes(rng_for(seed, 13, 1), N, K, 2)
+    sc = gen_scales(rng_for(seed, 13, 2), N, K, g)
+    r = gen_x(rng_for(seed, 13, 3), M, N)              # bf16 bit patterns
+    gt = gen_x(rng_for(seed, 13, 4), 1, N)[0]
+    return x, c, sc, g, r, gt
+
+
+def pin_residual_special_gates(o, seed=31):
+    """gate = 0 gives the residual exactly; residual = 0 and gate = 1 give the plain GEMM exactly."""
+    x, c, sc, g, r, _ = _residual_case(seed)
+    N = c.shape[0]
+    zero = _bf16_bits(np.zeros(N))
+    one = _bf16_bits(np.ones(N))
+    assert np.array_equal(o.residual_ref_f64(x, c, sc, g, r, zero), o.bf16_bits_to_f64(r))
+    rz = _bf16_bits(np.zeros(r.shape))
+    assert np.array_equal(o.residual_ref_f64(x, c, sc, g, rz, one), o.gemm_ref_f64(x, c, sc, g))
+
+
+def pin_residual_fsum(o, seed=33):
+    """Each element equals R + gate * (the correctly rounded sum of the exact products), R and gate
+    read from their bf16 bit patterns by hand (sign, exponent, mantissa)."""
+    x, c, sc, g, r, gt = _residual_case(seed)
+    y = o.residual_ref_f64(x, c, sc, g, r, gt)
+
+    def bf16(b):
+        b = int(b)
+        sgn = -1.0 if b >> 15 else 1.0
+        e, m = (b >> 7) & 0xFF, b & 0x7F
+        return sgn * (m / 128.0) * 2.0 ** -126 if e == 0 else sgn * (1 + m / 128.0) * 2.0 ** (e - 127)
+
+    for m in range(y.shape[0]):
+        for n in range(y.shape[1]):
+            want = bf16(r[m, n]) + bf16(gt[n]) * o.gemm_fsum_element(x, c, sc, g, m, n)
+            assert abs(y[m, n] - want) <= 1e-13 * (abs(want) + 1.0), (m, n, y[m, n], want)
+
+
+def pin_residual_gate_linearity(o, seed=35):
+    """Doubling the gate doubles Y - R exactly; the gate acts per output column (a one-hot gate
+    leaves every other column equal to R)."""
+    x, c, sc, g, r, gt = _residual_case(seed)
+    rf = o.bf16_bits_to_f64(r)
+    y1 = o.residual_ref_f64(x, c, sc, g, r, gt)
+    y2 = o.residual_ref_f64(x, c, sc, g, r, _bf16_bits(2.0 * o.bf16_bits_to_f64(gt)))
+    assert np.array_equal(y2 - rf, 2.0 * (y1 - rf))
+    N = c.shape[0]
+    hot = np.zeros(N)
+    hot[5] = 1.0
+    yh = o.residual_ref_f64(x, c, sc, g, r, _bf16_bits(hot))
+    others = np.arange(N) != 5
+    assert np.array_equal(yh[:, others], rf[:, others])
+    assert not np.array_equal(yh[:, 5], rf[:, 5])
+
+
+RESIDUAL_PINS = [pin_residual_special_gates, pin_residual_fsum, pin_residual_gate_linearity]

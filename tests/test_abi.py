@@ -111,6 +111,18 @@ def test_swiglu_rejects_before_touching_the_device():
     assert L.lowbit_gemm_swiglu(0, 0, 0, 0, 0, 256, 256, 64, 2, None) == OK            # M == 0
 
 
+def test_residual_rejects_before_touching_the_device():
+    """lowbit_gemm_residual validates as lowbit_gemm, plus its residual and gate pointers."""
+    L = _lib.lib()
+    assert L.lowbit_gemm_residual(A, A, A, A, A, A, 64, 250, 256, 64, 2, None) == INVALID      # N % 16
+    assert L.lowbit_gemm_residual(A, A, A, 0, A, A, 64, 256, 256, 64, 2, None) == INVALID      # null R
+    assert L.lowbit_gemm_residual(A, A, A, A, 0, A, 64, 256, 256, 64, 2, None) == INVALID      # null gate
+    assert L.lowbit_gemm_residual(A, A, A, A + 2, A, A, 64, 256, 256, 64, 2, None) == ALIGN
+    assert L.lowbit_gemm_residual(A, A, A, A, A + 2, A, 64, 256, 256, 64, 2, None) == ALIGN
+    assert L.lowbit_gemm_residual(A, A, A, A, A, A, 64, 256, 256, 32, 2, None) == UNSUPPORTED  # g = 32
+    assert L.lowbit_gemm_residual(0, 0, 0, 0, 0, 0, 0, 256, 256, 64, 2, None) == OK            # M == 0
+
+
 def test_variant_choice():
     """Tile choice: fewest rounds of tiles over 256 compute units, weighted by tile work.
     4608 x 3072 is 216 tiles of 256 x 256 (40 units idle) but exactly 256 of 288 x 192."""

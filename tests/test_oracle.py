@@ -10,7 +10,7 @@ from oracle import lowbit_ref as ref
 from tests import oracle_pins as P
 
 
-@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS, ids=lambda f: f.__name__)
 def test_pin_holds(pin):
     pin(P.real_oracle())
 
@@ -223,3 +223,37 @@ def test_roundtrip_large():
         w, bad = oracle.pack(c, bits)
         assert bad == 0 and w.shape == (96, 1024 * bits // 32)
         assert np.array_equal(oracle.unpack(w, 1024, bits), c)
+
+
+def _residual_gate_on_rows(x, c, s, g, r, gt):
+    """the gate indexed by output row m instead of feature n (M <= N in the pins)"""
+    y = oracle.gemm_ref_f64(x, c, s, g)
+    return oracle.bf16_bits_to_f64(r) + oracle.bf16_bits_to_f64(gt)[: y.shape[0], None] * y
+
+
+def _residual_no_gate(x, c, s, g, r, gt):
+    return oracle.bf16_bits_to_f64(r) + oracle.gemm_ref_f64(x, c, s, g)
+
+
+def _residual_gate_on_sum(x, c, s, g, r, gt):
+    gt_f = oracle.bf16_bits_to_f64(gt)[None, :]
+    return gt_f * (oracle.bf16_bits_to_f64(r) + oracle.gemm_ref_f64(x, c, s, g))
+
+
+RESIDUAL_PLANTED = {
+    "gate_dropped": dict(residual_ref_f64=_residual_no_gate),
+    "gate_on_rows": dict(residual_ref_f64=_residual_gate_on_rows),
+    "gate_scales_residual_too": dict(residual_ref_f64=_residual_gate_on_sum),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RESIDUAL_PLANTED))
+def test_residual_planted_mistake_is_caught(name):
+    broken = SimpleNamespace(**{**vars(P.real_oracle()), **RESIDUAL_PLANTED[name]})
+    failures = []
+    for pin in P.RESIDUAL_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every residual pin"
