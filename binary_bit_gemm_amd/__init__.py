@@ -89,6 +89,42 @@ def unpack(words, K: int, bits: int):
     return codes
 
 
+LAYOUT_GEMLITE_U8T = 1  # uint8 [K/4, N]: GemLite's int2 weights, packed over K with a transpose
+LAYOUT_MLX_U32 = 2      # uint32 [N, K/16]: MLX's packed rows
+
+
+def _import(src, layout: int, N: int, K: int, zero: int, count_invalid: bool):
+    torch = _torch()
+    words = torch.empty((N, words_per_row(K, 2)), dtype=torch.int32, device=src.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=src.device) if count_invalid else None
+    st = lib().lowbit_import_ternary(ctypes.c_void_p(src.data_ptr()), layout, zero, ctypes.c_void_p(words.data_ptr()),
+                                     N, K, ctypes.c_void_p(bad.data_ptr() if bad is not None else 0),
+                                     ctypes.c_void_p(_stream_ptr(src.device)))
+    _check(st, "lowbit_import_ternary")
+    return words, (int(bad.item()) if bad is not None else None)
+
+
+def import_gemlite(src, N: int, K: int, zero: int = 1, count_invalid: bool = True):
+    """GemLite int2 weights, uint8 [K/4, N] (transposed), levels q with code q - zero ->
+    (packed words [N, K/16] as int32, invalid count).  N and K are the caller's: the
+    orientation is never guessed from the buffer's shape, which is checked against them."""
+    torch = _torch()
+    _require(src, torch.uint8, "src")
+    if tuple(src.shape) != (K // 4, N) or K % 4:
+        raise ValueError(f"GemLite src must be uint8 [K/4, N] = ({K // 4}, {N}), got {tuple(src.shape)}")
+    return _import(src, LAYOUT_GEMLITE_U8T, N, K, zero, count_invalid)
+
+
+def import_mlx(src, N: int, K: int, zero: int = 1, count_invalid: bool = True):
+    """MLX 2-bit rows, uint32 (or int32) [N, K/16], levels q with code q - zero -> (packed words
+    [N, K/16] as int32, invalid count)."""
+    torch = _torch()
+    _require(src, torch.uint32 if src.dtype == torch.uint32 else torch.int32, "src")
+    if tuple(src.shape) != (N, K // 16) or K % 16:
+        raise ValueError(f"MLX src must be [N, K/16] = ({N}, {K // 16}), got {tuple(src.shape)}")
+    return _import(src, LAYOUT_MLX_U32, N, K, zero, count_invalid)
+
+
 def workspace_size(M: int, N: int, K: int, g: int = 64, bits: int = 2) -> int:
     """Bytes of workspace lowbit_gemm_ex can use for this shape (0: none needed)."""
     return int(lib().lowbit_workspace_size(M, N, K, g, bits))

@@ -37,6 +37,11 @@ hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, i
                        int32_t* bad_count, hipStream_t stream);
 hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
                          hipStream_t stream);
+// Ternary importers (import.hip): the layouts of include/lowbit.h's LOWBIT_LAYOUT_* values.
+constexpr int kLayoutGemliteU8T = 1;
+constexpr int kLayoutMlxU32 = 2;
+hipError_t launch_import(const void* src, int layout, int zero, uint32_t* W, int64_t N, int64_t K,
+                         int32_t* bad_count, hipStream_t stream);
 
 // Tiled MFMA kernels (LDS-staged X, packed weights and scales).  `variant` selects the tile;
 // TILE_288x192 and TILE_96x192 are the 16x16x32-block kernel (g = 64 or 128 only).

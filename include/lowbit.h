@@ -84,6 +84,35 @@ int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits
 int lowbit_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits, void* stream);
 
 /*
+ * lowbit_import_ternary -- ternary weights packed by another runtime -> packed words [N, K/16]
+ * in the format above (an offline, load-time step like lowbit_pack).
+ *   Both source layouts hold unsigned 2-bit levels q in {0, 1, 2, 3}, least significant field
+ *   first along K; the code is c = q - zero.  The pages name the layouts but not the level
+ *   coding: zero = 1 is the symmetric ternary form (q = 0, 1, 2 -> -1, 0, +1).
+ *   layout  LOWBIT_LAYOUT_GEMLITE_U8T: src is uint8 [K/4, N], transposed: byte (j, n) holds
+ *             codes k = 4j .. 4j+3 of output row n at bits 2(k%4) .. 2(k%4)+1 (GemLite's
+ *             int2 weights, packed over K with a transpose, shape (in_features / 4,
+ *             out_features): comment thread of the Bonsai-Image-Demo pull request "CPU
+ *             bring-up").  The shape, not a guess from the buffer, fixes the orientation: a
+ *             square weight is read as (K/4, N) like any other.
+ *           LOWBIT_LAYOUT_MLX_U32: src is uint32 [N, K/16], row-major by output feature:
+ *             word (n, j) holds codes k = 16j .. 16j+15 at bits 2(k%16) .. 2(k%16)+1 (packed
+ *             uint32 weights of the MLX checkpoint: "backend/ -- FastAPI Mac backend",
+ *             section "Checkpoint layout").  With MLX's affine groups w = s*q + b this
+ *             is exact when b = -zero*s; the library's scale is then s.
+ *   zero    0 .. 3.
+ *   W       device, N*K/16 uint32, written.
+ *   bad_count  device int32 or NULL: codes outside {-1, 0, +1} are packed as 0 and their
+ *           number is ADDED to *bad_count (the caller zeroes it).
+ *   Requires N % 16 == 0, K % 16 == 0, K <= 2^22, 16-byte aligned src and W.  Scales are not
+ *   touched: the library's fp16 [N, K/g] scales are the caller's.
+ */
+#define LOWBIT_LAYOUT_GEMLITE_U8T 1
+#define LOWBIT_LAYOUT_MLX_U32 2
+int lowbit_import_ternary(const void* src, int layout, int zero, uint32_t* W, int64_t N, int64_t K,
+                          int32_t* bad_count, void* stream);
+
+/*
  * lowbit_gemm -- Y[M, N] = X[M, K] . dequant(W)[N, K]^T, bf16 out (round to nearest even).
  *   X  device bf16 [M, K];  W  device packed words [N, K*bits/32];
  *   S  device fp16 [N, K/g];  Y  device bf16 [M, N], fully overwritten.

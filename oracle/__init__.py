@@ -16,6 +16,9 @@ define (see each docstring for the passage):
 * weights stored as packed uint32 words plus scales ("backend/ -- FastAPI Mac backend",
   section "Checkpoint layout": transformer-packed-mflux holds uint32 packed weights +
   scales);
+* other runtimes' ternary packs: GemLite's int2 weights, uint8 packed over K with a
+  transpose, (in_features / 4, out_features) (Bonsai-Image-Demo pull request 20, "CPU
+  bring-up"), and MLX's packed uint32 rows (the "Checkpoint layout" section above);
 * the reference computation is dequantise-to-dense followed by an ordinary matmul
   (Bonsai-Image-Demo pull request 20, "CPU image bring-up report": the validated CPU
   path runs the unpacked dense transformer).
@@ -31,5 +34,6 @@ from .lowbit_ref import (  # noqa: F401
     bf16_bits_to_f64, f64_to_bf16_bits_rne,
     pack, unpack, dequant_f64, gemm_ref_f64, gemm_ref_from_words, gemm_fsum_element,
     silu_f64, swiglu_ref_f64, residual_ref_f64,
+    gemlite_u8t_decode, gemlite_u8t_encode, mlx_u32_decode, mlx_u32_encode,
     check_tolerance, REL_FROB_TOL, ELEM_TOL,
 )

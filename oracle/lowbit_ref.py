@@ -30,6 +30,12 @@ R6  SwiGLU of the MLP-in linear (the MMDiT's 2 x 9216-output linear, mlx guide s
 R7  Gated residual of a block's output linear (the mlx guide's modulated MMDiT blocks,
     section "组件架构"): Y = R + gate[n] * (X . W^T)[m, n] with a per-feature gate; the exact
     form is a reading.
+R8  Importers of other runtimes' ternary packs: both hold unsigned 2-bit levels q, least
+    significant field first, with code c = q - zero (zero = 1 for the symmetric form; the
+    pages do not give the level coding).  GemLite: uint8 [K/4, N], byte (j, n) holding codes
+    k = 4j .. 4j+3 of row n (Bonsai-Image-Demo pull request 20, "CPU bring-up": packed over
+    K with a transpose, (in_features / 4, out_features)).  MLX: uint32 [N, K/16], word (n, j)
+    holding codes k = 16j .. 16j+15 ("backend/ -- FastAPI Mac backend", "Checkpoint layout").
 """
 from __future__ import annotations
 
@@ -130,6 +136,65 @@ def unpack(words: np.ndarray, K: int, bits: int) -> np.ndarray:
         else:
             out[:, :, i] = 2 * f.astype(np.int8) - 1
     return out.reshape(N, K)
+
+
+def _level_codes(q: np.ndarray, zero: int) -> Tuple[np.ndarray, int]:
+    """Unsigned levels -> ternary codes c = q - zero; codes outside {-1, 0, 1} become 0 and
+    are counted (reading R8)."""
+    c = q.astype(np.int64) - zero
+    bad = np.abs(c) > 1
+    c[bad] = 0
+    return c.astype(np.int8), int(np.count_nonzero(bad))
+
+
+def gemlite_u8t_decode(src: np.ndarray, N: int, K: int, zero: int = 1) -> Tuple[np.ndarray, int]:
+    """GemLite transposed uint8 [K/4, N] -> (int8 codes [N, K], invalid count): code k of
+    row n is the 2-bit level at bits 2*(k % 4) of byte (k // 4, n), minus `zero`."""
+    b = np.asarray(src, dtype=np.uint8)
+    if b.shape != (K // 4, N) or K % 4:
+        raise ValueError("GemLite src must be [K/4, N]")
+    q = np.zeros((N, K), dtype=np.uint8)
+    for k in range(K):
+        q[:, k] = (b[k // 4, :] >> (2 * (k % 4))) & 3
+    return _level_codes(q, zero)
+
+
+def mlx_u32_decode(src: np.ndarray, N: int, K: int, zero: int = 1) -> Tuple[np.ndarray, int]:
+    """MLX uint32 rows [N, K/16] -> (int8 codes [N, K], invalid count): code k of row n is the
+    2-bit level at bits 2*(k % 16) of word (n, k // 16), minus `zero`."""
+    w = np.asarray(src, dtype=np.uint32)
+    if w.shape != (N, K // 16) or K % 16:
+        raise ValueError("MLX src must be [N, K/16]")
+    q = np.zeros((N, K), dtype=np.uint32)
+    for k in range(K):
+        q[:, k] = (w[:, k // 16] >> np.uint32(2 * (k % 16))) & np.uint32(3)
+    return _level_codes(q, zero)
+
+
+def gemlite_u8t_encode(codes: np.ndarray, zero: int = 1) -> np.ndarray:
+    """int8 codes [N, K] -> GemLite transposed uint8 [K/4, N] with levels q = c + zero (0..3)."""
+    c = np.asarray(codes, dtype=np.int64)
+    N, K = c.shape
+    q = c + zero
+    if K % 4 or q.min(initial=0) < 0 or q.max(initial=0) > 3:
+        raise ValueError("levels must lie in 0..3 and K be a multiple of 4")
+    out = np.zeros((K // 4, N), dtype=np.uint8)
+    for k in range(K):
+        out[k // 4, :] |= (q[:, k] << (2 * (k % 4))).astype(np.uint8)
+    return out
+
+
+def mlx_u32_encode(codes: np.ndarray, zero: int = 1) -> np.ndarray:
+    """int8 codes [N, K] -> MLX uint32 rows [N, K/16] with levels q = c + zero (0..3)."""
+    c = np.asarray(codes, dtype=np.int64)
+    N, K = c.shape
+    q = c + zero
+    if K % 16 or q.min(initial=0) < 0 or q.max(initial=0) > 3:
+        raise ValueError("levels must lie in 0..3 and K be a multiple of 16")
+    out = np.zeros((N, K // 16), dtype=np.uint32)
+    for k in range(K):
+        out[:, k // 16] |= (q[:, k] << (2 * (k % 16))).astype(np.uint32)
+    return out
 
 
 # ----------------------------------------------------------------------------------------

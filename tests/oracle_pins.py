@@ -37,7 +37,9 @@ def real_oracle():
     return SimpleNamespace(pack=oracle.pack, unpack=oracle.unpack, dequant_f64=oracle.dequant_f64,
                            gemm_ref_f64=oracle.gemm_ref_f64, gemm_fsum_element=oracle.gemm_fsum_element,
                            bf16_bits_to_f64=oracle.bf16_bits_to_f64, silu_f64=oracle.silu_f64,
-                           swiglu_ref_f64=oracle.swiglu_ref_f64, residual_ref_f64=oracle.residual_ref_f64)
+                           swiglu_ref_f64=oracle.swiglu_ref_f64, residual_ref_f64=oracle.residual_ref_f64,
+                           gemlite_u8t_decode=oracle.gemlite_u8t_decode, gemlite_u8t_encode=oracle.gemlite_u8t_encode,
+                           mlx_u32_decode=oracle.mlx_u32_decode, mlx_u32_encode=oracle.mlx_u32_encode)
 
 
 # ----------------------------------------------------------------------------------------
@@ -327,3 +329,88 @@ def pin_residual_gate_linearity(o, seed=35):
 
 
 RESIDUAL_PINS = [pin_residual_special_gates, pin_residual_fsum, pin_residual_gate_linearity]
+
+
+# ----------------------------------------------------------------------------------------
+# Importers (GemLite transposed uint8, MLX uint32 rows; unsigned levels q, code q - zero)
+
+def pin_import_golden(o):
+    """Hand-worked bytes and words of the two source layouts (levels: 0 -> 00, 1 -> 01,
+    2 -> 10, least significant field first; zero = 1 maps codes -1, 0, +1 to levels 0, 1, 2)."""
+    z = np.zeros((16, 16), dtype=np.int8)
+    assert np.all(o.gemlite_u8t_encode(z) == 0x55)            # level 1 in all four fields
+    assert np.all(o.gemlite_u8t_encode(z + 1) == 0xAA)        # level 2
+    assert np.all(o.gemlite_u8t_encode(z - 1) == 0x00)        # level 0
+    one = z.copy()
+    one[2, 5] = -1                                            # row 2, k = 5: byte (1, 2), field 1
+    b = o.gemlite_u8t_encode(one)
+    assert b.shape == (4, 16) and b[1, 2] == 0x51 and np.count_nonzero(b != 0x55) == 1
+    codes, bad = o.gemlite_u8t_decode(b, 16, 16)
+    assert bad == 0 and np.array_equal(codes, one)
+    # a square source buffer (K/4 == N == 16): code (n = 0, k = 63) sits in byte (15, 0),
+    # field 3; read in the direct orientation it would land in row 15
+    sq = np.full((16, 16), 0x55, dtype=np.uint8)
+    sq[15, 0] = 0x95                                          # 10 01 01 01
+    codes, bad = o.gemlite_u8t_decode(sq, 16, 64)
+    assert bad == 0 and codes[0, 63] == 1 and np.count_nonzero(codes) == 1
+    # MLX rows
+    z = np.zeros((16, 32), dtype=np.int8)
+    assert np.all(o.mlx_u32_encode(z) == 0x55555555)
+    one = z.copy()
+    one[0, 0] = 1
+    one[1, 31] = -1                                           # word (1, 1), field 15 -> level 0
+    w = o.mlx_u32_encode(one)
+    assert w[0, 0] == 0x55555556 and w[1, 1] == 0x15555555 and np.count_nonzero(w != 0x55555555) == 2
+    codes, bad = o.mlx_u32_decode(w, 16, 32)
+    assert bad == 0 and np.array_equal(codes, one)
+    # level 3 is no ternary code at zero = 1; at zero = 3 levels 0 .. 2 are the invalid ones
+    codes, bad = o.gemlite_u8t_decode(np.full((4, 16), 0xFF, dtype=np.uint8), 16, 16)
+    assert bad == 256 and not codes.any()
+    codes, bad = o.gemlite_u8t_decode(np.full((4, 16), 0xFF, dtype=np.uint8), 16, 16, zero=3)
+    assert bad == 0 and not codes.any()
+    codes, bad = o.mlx_u32_decode(np.full((16, 1), 0x00000001, dtype=np.uint32), 16, 16, zero=0)
+    assert bad == 0 and np.all(codes[:, 0] == 1) and not codes[:, 1:].any()
+    codes, bad = o.mlx_u32_decode(np.full((16, 1), 0x00000001, dtype=np.uint32), 16, 16, zero=3)
+    assert bad == 16 * 16 and not codes.any()
+
+
+def pin_import_other_routes(o, seed=41):
+    """The decoders against routes written differently: the library's field of code q - 1 is
+    (q + 2) mod 3 (levels 0, 1, 2 -> fields 10, 00, 01), read from base-4 digits of Python
+    integers; GemLite bytes through numpy's little-endian unpackbits and a transpose."""
+    rng = np.random.default_rng(seed)
+    N, K = 32, 96
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    w = o.mlx_u32_encode(codes)
+    got, bad = o.mlx_u32_decode(w, N, K)
+    assert bad == 0 and np.array_equal(got, codes)
+    packed, _ = o.pack(got, 2)
+    for n in range(N):
+        for j in range(K // 16):
+            v, expect = int(w[n, j]), 0
+            for i in range(16):
+                v, q = divmod(v, 4)
+                expect += ((q + 2) % 3) * 4 ** i
+            assert int(packed[n, j]) == expect
+    b = o.gemlite_u8t_encode(codes)
+    bits = np.unpackbits(b[:, :, None], axis=2, bitorder="little")          # [K/4, N, 8]
+    levels = (bits[:, :, 0::2] + 2 * bits[:, :, 1::2]).astype(np.int64)     # [K/4, N, 4]
+    direct = levels.transpose(0, 2, 1).reshape(K, N).T - 1
+    assert np.array_equal(direct, codes)
+    got, bad = o.gemlite_u8t_decode(b, N, K)
+    assert bad == 0 and np.array_equal(got, codes)
+
+
+def pin_import_layouts_agree(o, seed=43):
+    """The same weight through either layout decodes to the same codes, at every zero point
+    whose levels fit in 2 bits."""
+    rng = np.random.default_rng(seed)
+    N, K = 48, 64
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    for zero in (1, 2):
+        a, ba = o.gemlite_u8t_decode(o.gemlite_u8t_encode(codes, zero), N, K, zero)
+        m, bm = o.mlx_u32_decode(o.mlx_u32_encode(codes, zero), N, K, zero)
+        assert ba == bm == 0 and np.array_equal(a, codes) and np.array_equal(m, codes)
+
+
+IMPORT_PINS = [pin_import_golden, pin_import_other_routes, pin_import_layouts_agree]

@@ -123,6 +123,23 @@ def test_residual_rejects_before_touching_the_device():
     assert L.lowbit_gemm_residual(0, 0, 0, 0, 0, 0, 0, 256, 256, 64, 2, None) == OK            # M == 0
 
 
+def test_import_rejects_before_touching_the_device():
+    """lowbit_import_ternary validates layout, zero point, shape, size and alignment first."""
+    L = _lib.lib()
+    GL, MLX = lb.LAYOUT_GEMLITE_U8T, lb.LAYOUT_MLX_U32
+    assert (GL, MLX) == (1, 2)
+    assert L.lowbit_import_ternary(A, 3, 1, A, 64, 256, None, None) == INVALID                  # layout
+    assert L.lowbit_import_ternary(A, GL, 4, A, 64, 256, None, None) == INVALID                 # zero
+    assert L.lowbit_import_ternary(A, GL, -1, A, 64, 256, None, None) == INVALID
+    assert L.lowbit_import_ternary(A, GL, 1, A, 40, 256, None, None) == INVALID                 # N % 16
+    assert L.lowbit_import_ternary(A, MLX, 1, A, 64, 264, None, None) == INVALID                # K % 16
+    assert L.lowbit_import_ternary(A, GL, 1, A, 16, (1 << 22) + 16, None, None) == UNSUPPORTED  # K > 2^22
+    assert L.lowbit_import_ternary(0, GL, 1, A, 64, 256, None, None) == INVALID                 # null src
+    assert L.lowbit_import_ternary(A + 4, GL, 1, A, 64, 256, None, None) == ALIGN
+    assert L.lowbit_import_ternary(A, MLX, 1, A + 8, 64, 256, None, None) == ALIGN
+    assert L.lowbit_import_ternary(0, GL, 1, 0, 0, 256, None, None) == OK                       # empty
+
+
 def test_variant_choice():
     """Tile choice: fewest rounds of tiles over 256 compute units, weighted by tile work.
     4608 x 3072 is 216 tiles of 256 x 256 (40 units idle) but exactly 256 of 288 x 192."""

@@ -10,7 +10,8 @@ from oracle import lowbit_ref as ref
 from tests import oracle_pins as P
 
 
-@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS + P.IMPORT_PINS,
+                         ids=lambda f: f.__name__)
 def test_pin_holds(pin):
     pin(P.real_oracle())
 
@@ -257,3 +258,73 @@ def test_residual_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError):
             failures.append(pin.__name__)
     assert failures, f"planted mistake {name} passed every residual pin"
+
+
+# planted importer mistakes: each changes the decoder and its matching encoder alike, so a
+# round trip alone would not see it
+
+
+def _gl_msb_decode(src, N, K, zero=1):
+    b = np.asarray(src, dtype=np.uint8)
+    q = np.stack([(b[k // 4, :] >> (6 - 2 * (k % 4))) & 3 for k in range(K)], axis=1)
+    return ref._level_codes(q, zero)
+
+
+def _gl_msb_encode(codes, zero=1):
+    c = np.asarray(codes, dtype=np.int64) + zero
+    out = np.zeros((c.shape[1] // 4, c.shape[0]), dtype=np.uint8)
+    for k in range(c.shape[1]):
+        out[k // 4, :] |= (c[:, k] << (6 - 2 * (k % 4))).astype(np.uint8)
+    return out
+
+
+def _gl_direct_decode(src, N, K, zero=1):
+    b = np.asarray(src, dtype=np.uint8).reshape(N, K // 4)  # the orientation trap
+    q = np.stack([(b[:, k // 4] >> (2 * (k % 4))) & 3 for k in range(K)], axis=1)
+    return ref._level_codes(q, zero)
+
+
+def _gl_direct_encode(codes, zero=1):
+    c = np.asarray(codes, dtype=np.int64) + zero
+    N, K = c.shape
+    out = np.zeros((N, K // 4), dtype=np.uint8)
+    for k in range(K):
+        out[:, k // 4] |= (c[:, k] << (2 * (k % 4))).astype(np.uint8)
+    return out.reshape(K // 4, N)
+
+
+def _mlx_sign_decode(src, N, K, zero=1):
+    codes, bad = oracle.mlx_u32_decode(src, N, K, zero)
+    return -codes, bad
+
+
+def _mlx_sign_encode(codes, zero=1):
+    return oracle.mlx_u32_encode(-np.asarray(codes, dtype=np.int8), zero)
+
+
+def _mlx_word_order_decode(src, N, K, zero=1):
+    return oracle.mlx_u32_decode(np.asarray(src)[:, ::-1], N, K, zero)
+
+
+def _mlx_word_order_encode(codes, zero=1):
+    return np.ascontiguousarray(oracle.mlx_u32_encode(codes, zero)[:, ::-1])
+
+
+IMPORT_PLANTED = {
+    "gemlite_msb_first": dict(gemlite_u8t_decode=_gl_msb_decode, gemlite_u8t_encode=_gl_msb_encode),
+    "gemlite_direct_orientation": dict(gemlite_u8t_decode=_gl_direct_decode, gemlite_u8t_encode=_gl_direct_encode),
+    "mlx_code_sign": dict(mlx_u32_decode=_mlx_sign_decode, mlx_u32_encode=_mlx_sign_encode),
+    "mlx_word_order": dict(mlx_u32_decode=_mlx_word_order_decode, mlx_u32_encode=_mlx_word_order_encode),
+}
+
+
+@pytest.mark.parametrize("name", sorted(IMPORT_PLANTED))
+def test_import_planted_mistake_is_caught(name):
+    broken = SimpleNamespace(**{**vars(P.real_oracle()), **IMPORT_PLANTED[name]})
+    failures = []
+    for pin in P.IMPORT_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every import pin"
