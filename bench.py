@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
                     choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu",
-                             "swiglu16", "residual"])
+                             "swiglu16", "residual", "te4"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -127,6 +127,11 @@ def problems_for(workload):
     if workload == "residual":
         # the MLP-out linear at 1024^2 (M = 4608, 9216 -> 3072) with its gated residual update fused
         return [W.Problem("m4608_mlp_out_residual", 4608, 3072, 9216, W.TERNARY, 64, 3, 3)]
+    if workload == "te4":
+        # the 4-bit text encoder's MLP at a 512-token prompt (hidden 2560, intermediate 9728): gate
+        # and up fused into one 2560 -> 19456 linear, then down 9728 -> 2560; two dependent launches
+        return [W.Problem("te_mlp_gate_up", 512, 19456, 2560, W.INT4, 64, 6, 0),
+                W.Problem("te_mlp_down", 512, 2560, 9728, W.INT4, 64, 6, 1)]
     if workload == "swiglu16":
         # the same linear at M = 16 (the skinny denoise-step row count)
         return [W.Problem("m16_mlp_in_swiglu", 16, 18432, 3072, W.TERNARY, 64, 3, 2)]

@@ -383,8 +383,7 @@ int pick_ncb(const GemmProblem* probs, int count) {
 }  // namespace
 
 bool skinny_supported(int g, int bits) {
-    (void)bits;
-    return g == 32 || g == 64 || g == 128;
+    return (bits == 1 || bits == 2) && (g == 32 || g == 64 || g == 128);
 }
 
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits) {

@@ -1,4 +1,4 @@
-// Packed ternary or binary GEMM on 16x16x32 MFMA blocks: Y[M,N] = X[M,K] . dequant(W)[N,K]^T,
+// Packed ternary, binary or 4-bit GEMM on 16x16x32 MFMA blocks: Y[M,N] = X[M,K] . dequant(W)[N,K]^T,
 // for scale groups of 64 or 128.
 //
 // Why a second tile kernel: with 32x32 blocks a workgroup tile is a multiple of 32 in both
@@ -28,7 +28,8 @@
 // neighbouring chunks of each activation row.  Its codes are then the low (q even) or high
 // (q odd) halves of two consecutive ternary words (codes 32 (q >> 1) + 16 i + 8 (q & 1) ..),
 // or bytes (q & 1) and (q & 1) + 2 of binary word q >> 1; one 8-byte read of the row's step
-// words and one byte permute gather them.
+// words and one byte permute gather them.  4-bit codes (8 per word) make each chunk one word:
+// the lane reads words phi(q, 0) and phi(q, 0) + 2 of the step (one two-dword LDS read).
 #include "lowbit_device.h"
 #include "lowbit_internal.h"
 
@@ -66,7 +67,7 @@ struct Cfg16 {
     static constexpr int W_STEP = KS * BITS / 8;             // packed bytes per row and step
     static constexpr int W_SPB = kWB / W_STEP;               // steps per weight block
     static_assert(G == 64 || G == 128, "scale groups of 64 or 128");
-    static_assert(BITS == 1 || BITS == 2, "binary or ternary codes");
+    static_assert(BITS == 1 || BITS == 2 || BITS == 4, "binary, ternary or 4-bit codes");
 };
 
 // EPI = kEpiSwiglu: the problem's W and S hold 2N rows, gate rows [0, N) then up rows [N, 2N), and
@@ -234,14 +235,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
             const int r = wn0 + nb * 16 + l16;
-            const int byte0 = wj * C::W_STEP;  // the step's bytes within the block row
-            o.w[nb] = *reinterpret_cast<const u32x2_t*>(wt + w_rd[nb] + (w_pos(r, byte0 >> 4) << 4) + (byte0 & 15));
-            // x 1/2 (ternary: the operand holds 2c) or x -1/2 (binary: -2c).  Also keeps the
+            if constexpr (BITS == 4) {
+                // words phi(q, 0) and phi(q, 1) = phi(q, 0) + 2 of the step: dwords q & 1 and
+                // (q & 1) + 2 of the step's 16-byte chunk q >> 1
+                const int byte0 = wj * C::W_STEP + 16 * (q >> 1);
+                const unsigned char* b = wt + w_rd[nb] + (w_pos(r, byte0 >> 4) << 4) + 4 * (q & 1);
+                o.w[nb] = u32x2_t{*reinterpret_cast<const uint32_t*>(b), *reinterpret_cast<const uint32_t*>(b + 8)};
+            } else {
+                const int byte0 = wj * C::W_STEP;  // the step's bytes within the block row
+                o.w[nb] = *reinterpret_cast<const u32x2_t*>(wt + w_rd[nb] + (w_pos(r, byte0 >> 4) << 4) + (byte0 & 15));
+            }
+            // x 1/2 (ternary: the operand holds 2c), x -1/2 (binary: -2c) or x 1/16 (4-bit: 16c).  Also keeps the
             // conversion out of the FMA (an fp16 operand makes it v_fma_mix_f32, whose result
             // does not share the accumulator's register and doubles the accumulator registers
             // across the unrolled steps).
             o.sc[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + grp_in_block * 2)) *
-                       (BITS == 2 ? 0.5f : -0.5f);
+                       (BITS == 2 ? 0.5f : BITS == 4 ? 0.0625f : -0.5f);
         }
     };
 
@@ -253,11 +262,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         u32x4_t bfr[C::NB][2];
         auto expand = [&](int nb) {
             uint32_t d[8];
-            const uint32_t codes = perm_b32(o.w[nb][1], o.w[nb][0], gather_sel);
-            if constexpr (BITS == 2)
-                expand_ternary_word(codes, d);
-            else
-                expand_binary_16(codes, two_pair, d);
+            if constexpr (BITS == 4) {
+                expand_int4_word(o.w[nb][0], d);
+                expand_int4_word(o.w[nb][1], d + 4);
+            } else {
+                const uint32_t codes = perm_b32(o.w[nb][1], o.w[nb][0], gather_sel);
+                if constexpr (BITS == 2)
+                    expand_ternary_word(codes, d);
+                else
+                    expand_binary_16(codes, two_pair, d);
+            }
             bfr[nb][0] = u32x4_t{d[0], d[1], d[2], d[3]};
             bfr[nb][1] = u32x4_t{d[4], d[5], d[6], d[7]};
         };
@@ -479,7 +493,7 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
 
 }  // namespace
 
-bool tile16_supported(int g, int bits) { return (bits == 1 || bits == 2) && (g == 64 || g == 128); }
+bool tile16_supported(int g, int bits) { return (bits == 1 || bits == 2 || bits == 4) && (g == 64 || g == 128); }
 
 template <int G, int BITS>
 hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hipStream_t stream) {
@@ -509,6 +523,8 @@ template <int EPI>
 hipError_t launch_epi16_gb(const GemmProblem* probs, int count, int g, int bits, hipStream_t stream) {
     if (bits == 2)
         return g == 64 ? launch_epi16<64, 2, EPI>(probs, count, stream) : launch_epi16<128, 2, EPI>(probs, count, stream);
+    if (bits == 4)
+        return g == 64 ? launch_epi16<64, 4, EPI>(probs, count, stream) : launch_epi16<128, 4, EPI>(probs, count, stream);
     return g == 64 ? launch_epi16<64, 1, EPI>(probs, count, stream) : launch_epi16<128, 1, EPI>(probs, count, stream);
 }
 
@@ -525,6 +541,9 @@ hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, 
     if (bits == 2)
         return g == 64 ? launch_variant16<64, 2>(probs, count, variant, stream)
                        : launch_variant16<128, 2>(probs, count, variant, stream);
+    if (bits == 4)
+        return g == 64 ? launch_variant16<64, 4>(probs, count, variant, stream)
+                       : launch_variant16<128, 4>(probs, count, variant, stream);
     return g == 64 ? launch_variant16<64, 1>(probs, count, variant, stream)
                    : launch_variant16<128, 1>(probs, count, variant, stream);
 }

@@ -389,11 +389,12 @@ constexpr TileShape kTiles[] = {
 }  // namespace
 
 int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
-    int best = TILE_64x256;
+    int best = bits == 4 ? TILE_288x192 : TILE_64x256;
     double best_cost = 0.0;
     for (const TileShape& t : kTiles) {
         if (is_tile16_variant(t.variant) && !tile16_supported(g, bits)) continue;
-        if (t.variant == TILE_96x192 || t.variant == TILE_96x192K2) {
+        if (bits == 4 && !is_tile16_variant(t.variant)) continue;  // 4-bit codes: the 16x16-block tile only
+        if ((t.variant == TILE_96x192 || t.variant == TILE_96x192K2) && bits != 4) {
             // measured at M = 1536; below M = 1024 they stay unused.  The K split needs an even
             // number of 64-element steps.
             bool skip = false;
@@ -435,6 +436,7 @@ const char* tile_variant_name(int variant) {
 
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream) {
+    if (bits == 4 && !is_tile16_variant(variant)) variant = TILE_288x192;  // the only 4-bit kernel
     if (is_tile16_variant(variant)) {
         if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, bits, variant, stream);
         variant = TILE_256x256;

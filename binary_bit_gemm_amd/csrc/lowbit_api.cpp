@@ -32,7 +32,7 @@ constexpr int64_t kMaxOutputs = int64_t(1) << 37;
 constexpr int64_t kMaxCodes = int64_t(1) << 40;
 
 int check_pack_args(const void* codes, const void* W, int64_t N, int64_t K, int bits) {
-    if (bits != 1 && bits != 2) return LOWBIT_E_UNSUPPORTED;
+    if (bits != 1 && bits != 2 && bits != 4) return LOWBIT_E_UNSUPPORTED;
     if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return LOWBIT_E_INVALID;
     if (K % (32 / bits) != 0) return LOWBIT_E_INVALID;
     if (N * K > kMaxCodes) return LOWBIT_E_UNSUPPORTED;
@@ -120,7 +120,7 @@ int launch_one(const lowbit::GemmProblem& p, int g, int bits, hipStream_t stream
 // Calls f(group, n, g, bits) for the problems of each (g, bits) class with M, N, K > 0.
 template <class F>
 int for_each_class(const lowbit_problem* problems, int count, F&& f) {
-    static const int kClasses[6][2] = {{64, 2}, {64, 1}, {128, 2}, {128, 1}, {32, 2}, {32, 1}};
+    static const int kClasses[8][2] = {{64, 2}, {64, 1}, {128, 2}, {128, 1}, {32, 2}, {32, 1}, {64, 4}, {128, 4}};
     lowbit::GemmProblem grp[LOWBIT_MAX_BATCH];
     for (const auto& cls : kClasses) {
         int n = 0;
@@ -175,7 +175,7 @@ const char* lowbit_status_string(int status) {
     switch (status) {
         case LOWBIT_OK: return "ok";
         case LOWBIT_E_INVALID: return "invalid argument (null pointer, bad size, N % 16 or K % g != 0)";
-        case LOWBIT_E_UNSUPPORTED: return "unsupported (bits must be 1 or 2, g one of 32/64/128, device gfx950)";
+        case LOWBIT_E_UNSUPPORTED: return "unsupported (bits must be 1, 2 or 4, g one of 32/64/128 (4-bit: 64/128), device gfx950)";
         case LOWBIT_E_ALIGN: return "tensor pointer not 16-byte aligned";
         case LOWBIT_E_HIP: return "HIP runtime error (see lowbit_last_hip_error)";
         case LOWBIT_E_TOO_MANY: return "too many problems in one batched call";
@@ -204,8 +204,9 @@ int lowbit_device_supported(int device) {
 
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,
                            int64_t M, int64_t N, int64_t K, int g, int bits) {
-    if (bits != 1 && bits != 2) return LOWBIT_E_UNSUPPORTED;
+    if (bits != 1 && bits != 2 && bits != 4) return LOWBIT_E_UNSUPPORTED;
     if (g != 32 && g != 64 && g != 128) return LOWBIT_E_UNSUPPORTED;
+    if (bits == 4 && g == 32) return LOWBIT_E_UNSUPPORTED;  // 4-bit codes run on the 16x16-block tile only
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return LOWBIT_E_INVALID;
     if (K % g != 0 || N % 16 != 0) return LOWBIT_E_INVALID;
     if (K > kMaxK || N * K / 8 * bits > kMaxWeightBytes || M * N > kMaxOutputs) return LOWBIT_E_UNSUPPORTED;
@@ -221,6 +222,7 @@ const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits
     int v = choose_variant(M, N, K, g, bits);
     if (v == 100) return "skinny";
     if (v == 102) return "resident";
+    if (bits == 4 && !lowbit::is_tile16_variant(v)) v = lowbit::TILE_288x192;  // as launch_gemm_tiled_group
     if (lowbit::is_tile16_variant(v) && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
     return lowbit::tile_variant_name(v);
 }

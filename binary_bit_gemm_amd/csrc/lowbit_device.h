@@ -34,6 +34,21 @@ __device__ __forceinline__ constexpr uint32_t pair_sel(int b) {
 //   e_r  = fields r, r+4, r+8, r+12 moved to the low bits of bytes 0..3
 //   l_r  = table lookup of each byte: 0 -> 0x00, 1 -> 0x40, 2 -> 0xC0, 3 -> 0x00
 //   out  = byte gathers from l_r (codes 4b+r sit in byte b of l_r)
+// 8 signed 4-bit codes (two's complement, code i at bits 4i .. 4i+3) -> 8 bf16 of 16 * code;
+// out[j] holds codes 2j (low half) and 2j + 1 (high half).  Each code moves to the top nibble
+// of a byte, whose signed value is 16 * code; its fp32 conversion is exact, and so is the bf16
+// taken as the upper half of that fp32 (16 * code has at most 4 significant bits).
+__device__ __forceinline__ void expand_int4_word(uint32_t w, uint32_t out[4]) {
+    const uint32_t ev = (w << 4) & 0xF0F0F0F0u;  // codes 0, 2, 4, 6
+    const uint32_t od = w & 0xF0F0F0F0u;         // codes 1, 3, 5, 7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float fe = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
+        const float fo = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
+        out[j] = perm_b32(__float_as_uint(fo), __float_as_uint(fe), 0x07060302u);
+    }
+}
+
 __device__ __forceinline__ void expand_ternary_word(uint32_t w, uint32_t out[8]) {
     constexpr uint32_t kHighByte = 0x00C04000u;
     const uint32_t e0 = w & 0x03030303u;

@@ -1,8 +1,9 @@
 // Packing and unpacking of weight codes (offline / load-time steps).
 //
 // One thread per output uint32 word.  Ternary: 16 int8 codes -> 2-bit fields
-// (00 -> 0, 01 -> +1, 10 -> -1), binary: 32 codes -> bits (1 -> +1, 0 -> -1), least
-// significant field first along K.  Invalid codes pack as 0 bits and are counted.
+// (00 -> 0, 01 -> +1, 10 -> -1), binary: 32 codes -> bits (1 -> +1, 0 -> -1), 4-bit: 8 codes
+// in [-8, 7] -> two's complement nibbles; least significant field first along K.  Invalid
+// codes pack as 0 bits and are counted.
 #include "lowbit_internal.h"
 
 namespace lowbit {
@@ -26,7 +27,18 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* __restrict
     constexpr int kPer = 32 / BITS;
     const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     int bad = 0;
-    if (i < nwords) {
+    if (BITS == 4 && i < nwords) {
+        const uint2 v = *reinterpret_cast<const uint2*>(codes + i * kPer);
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = int(int8_t((k < 4 ? v.x : v.y) >> (8 * (k & 3))));
+            const bool ok = c >= -8 && c <= 7;
+            bad += !ok;
+            word |= (ok ? uint32_t(c) & 0xFu : 0u) << (4 * k);
+        }
+        W[i] = word;
+    } else if (i < nwords) {
         // Codes of word i are contiguous: [i*kPer, (i+1)*kPer) of the row-major [N, K] array.
         const uint4* src = reinterpret_cast<const uint4*>(codes + i * kPer);
         uint32_t word = 0;
@@ -69,6 +81,16 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __rest
     const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     if (i >= nwords) return;
     const uint32_t w = W[i];
+    if constexpr (BITS == 4) {
+        uint32_t parts[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = int(w << (28 - 4 * k)) >> 28;  // sign-extended nibble k
+            parts[k >> 2] |= (uint32_t(c) & 0xFFu) << (8 * (k & 3));
+        }
+        *reinterpret_cast<uint2*>(codes + i * kPer) = make_uint2(parts[0], parts[1]);
+        return;
+    }
     uint4* dst = reinterpret_cast<uint4*>(codes + i * kPer);
 #pragma unroll
     for (int v = 0; v < kPer / 16; ++v) {
@@ -101,7 +123,9 @@ hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, i
     const int64_t nwords = N * K * bits / 32;
     if (nwords == 0) return hipSuccess;
     const dim3 grid(unsigned((nwords + kThreads - 1) / kThreads));
-    if (bits == 2)
+    if (bits == 4)
+        hipLaunchKernelGGL(pack_kernel<4>, grid, dim3(kThreads), 0, stream, codes, W, nwords, bad_count);
+    else if (bits == 2)
         hipLaunchKernelGGL(pack_kernel<2>, grid, dim3(kThreads), 0, stream, codes, W, nwords, bad_count);
     else
         hipLaunchKernelGGL(pack_kernel<1>, grid, dim3(kThreads), 0, stream, codes, W, nwords, bad_count);
@@ -113,7 +137,9 @@ hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K,
     const int64_t nwords = N * K * bits / 32;
     if (nwords == 0) return hipSuccess;
     const dim3 grid(unsigned((nwords + kThreads - 1) / kThreads));
-    if (bits == 2)
+    if (bits == 4)
+        hipLaunchKernelGGL(unpack_kernel<4>, grid, dim3(kThreads), 0, stream, W, codes, nwords);
+    else if (bits == 2)
         hipLaunchKernelGGL(unpack_kernel<2>, grid, dim3(kThreads), 0, stream, W, codes, nwords);
     else
         hipLaunchKernelGGL(unpack_kernel<1>, grid, dim3(kThreads), 0, stream, W, codes, nwords);

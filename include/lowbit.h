@@ -25,6 +25,10 @@
  *       written; readers decode it as 0.
  *   binary  (bits = 1): 32 codes per uint32, along K: code k of row n is bit k%32 of
  *       W[n * (K/32) + k/32];  1 -> +1, 0 -> -1.
+ *   4-bit   (bits = 4): 8 codes per uint32, along K: code k of row n is the two's complement
+ *       nibble at bits 4*(k%8) .. 4*(k%8)+3 of W[n * (K/8) + k/8], values -8 .. 7 (the 4-bit
+ *       text encoder of the binary model card's "Model Overview" table; the card gives no
+ *       zero point, so the form is the same symmetric w = s * c).
  *   scales: fp16 (IEEE binary16) S[n * (K/g) + k/g], symmetric (no zero point).
  * Activations X[M, K] and outputs Y[M, N] are bf16, row-major, contiguous.
  *
@@ -35,7 +39,7 @@
  *     caller's next synchronisation.
  *   - Arguments are validated on the host before anything is enqueued; a non-zero
  *     return means nothing was launched.
- *   - Supported: bits in {1, 2}; g in {32, 64, 128}; K % g == 0; N % 16 == 0; M >= 0
+ *   - Supported: bits in {1, 2, 4} (4: g in {64, 128} only); g in {32, 64, 128}; K % g == 0; N % 16 == 0; M >= 0
  *     (M == 0 or N == 0 is a no-op); M, N < 2^31; K <= 2^22; packed weights under 4 GiB
  *     (N*K*bits/8 < 2^32); M*N <= 2^37; the current device is gfx950.  lowbit_pack and
  *     lowbit_unpack take N*K <= 2^40 codes.  Shapes past these limits return
@@ -68,11 +72,12 @@ enum {
 
 /*
  * lowbit_pack -- int8 codes [N, K] -> packed words [N, K*bits/32] in the format above.
- *   codes       device, N*K int8, row-major.  Ternary expects {-1,0,1}, binary {-1,1}.
+ *   codes       device, N*K int8, row-major.  Ternary expects {-1,0,1}, binary {-1,1},
+ *               4-bit -8 .. 7.
  *   W           device, N*K*bits/32 uint32, written.
  *   bad_count   device int32 or NULL.  When given, the number of codes outside the
  *               valid set is ADDED to *bad_count (the caller zeroes it); such codes are
- *               packed as 0 bits (ternary 0, binary -1).
+ *               packed as 0 bits (ternary 0, binary -1, 4-bit 0).
  *   Requires K % (32/bits) == 0.  This is the offline, load-time step.
  */
 int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,

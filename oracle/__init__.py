@@ -30,7 +30,7 @@ Parity status: every function here is pinned by tests/test_oracle.py (golden wor
 brute-force bit strings, math.fsum dot products, closed forms, a library matmul).
 """
 from .lowbit_ref import (  # noqa: F401
-    TERNARY, BINARY,
+    TERNARY, BINARY, INT4,
     bf16_bits_to_f64, f64_to_bf16_bits_rne,
     pack, unpack, dequant_f64, gemm_ref_f64, gemm_ref_from_words, gemm_fsum_element,
     silu_f64, swiglu_ref_f64, residual_ref_f64,

@@ -36,6 +36,10 @@ R8  Importers of other runtimes' ternary packs: both hold unsigned 2-bit levels 
     k = 4j .. 4j+3 of row n (Bonsai-Image-Demo pull request 20, "CPU bring-up": packed over
     K with a transpose, (in_features / 4, out_features)).  MLX: uint32 [N, K/16], word (n, j)
     holding codes k = 16j .. 16j+15 ("backend/ -- FastAPI Mac backend", "Checkpoint layout").
+R9  4-bit codes (the 4-bit text encoder of the binary model card's "Model Overview" table):
+    integers c in [-8, 7] as two's complement nibbles, 8 per uint32 along K, least significant
+    first (code k at bits 4*(k % 8) of word k // 8), with the symmetric form w = s * c of R4.
+    The card names only "4-bit HQQ"; its zero points are not on the pages.
 """
 from __future__ import annotations
 
@@ -46,6 +50,7 @@ import numpy as np
 
 TERNARY = 2
 BINARY = 1
+INT4 = 4
 
 REL_FROB_TOL = 5e-3
 ELEM_TOL = 1e-2
@@ -95,16 +100,21 @@ def pack(codes: np.ndarray, bits: int) -> Tuple[np.ndarray, int]:
     """int8 codes [N, K] -> (uint32 words [N, K*bits/32], number of invalid codes).
 
     Ternary: field(c) = 01 for +1, 10 for -1, 00 for 0, placed at bits 2*(k % 16) of word
-    k // 16.  Binary: bit 1 for +1, bit 0 for -1, at bit k % 32 of word k // 32."""
+    k // 16.  Binary: bit 1 for +1, bit 0 for -1, at bit k % 32 of word k // 32.  4-bit: the
+    nibble c mod 16 (two's complement) at bits 4*(k % 8) of word k // 8 (reading R9)."""
     c = np.asarray(codes, dtype=np.int8)
     if c.ndim != 2:
         raise ValueError("codes must be 2-D [N, K]")
     N, K = c.shape
     per_word = 32 // bits
-    if bits not in (TERNARY, BINARY) or K % per_word:
-        raise ValueError("bits must be 1 or 2 and K a multiple of 32/bits")
+    if bits not in (TERNARY, BINARY, INT4) or K % per_word:
+        raise ValueError("bits must be 1, 2 or 4 and K a multiple of 32/bits")
     field = np.zeros((N, K), dtype=np.uint32)
-    if bits == TERNARY:
+    if bits == INT4:
+        ok = (c >= -8) & (c <= 7)
+        field[ok] = (c[ok].astype(np.int64) % 16).astype(np.uint32)
+        bad = int(np.count_nonzero(~ok))
+    elif bits == TERNARY:
         field[c == 1] = 1
         field[c == -1] = 2
         bad = int(np.count_nonzero((c != 0) & (c != 1) & (c != -1)))
@@ -122,7 +132,7 @@ def unpack(words: np.ndarray, K: int, bits: int) -> np.ndarray:
     """uint32 words [N, K*bits/32] -> int8 codes [N, K].
 
     Ternary: c = (f & 1) - ((f >> 1) & 1) for each 2-bit field f (so 11 decodes to 0).
-    Binary: c = 2 * bit - 1."""
+    Binary: c = 2 * bit - 1.  4-bit: c = f - 16 for nibbles f >= 8, else f."""
     w = np.asarray(words, dtype=np.uint32)
     per_word = 32 // bits
     N = w.shape[0]
@@ -131,7 +141,9 @@ def unpack(words: np.ndarray, K: int, bits: int) -> np.ndarray:
     out = np.zeros((N, w.shape[1], per_word), dtype=np.int8)
     for i in range(per_word):
         f = (w >> np.uint32(bits * i)) & np.uint32((1 << bits) - 1)
-        if bits == TERNARY:
+        if bits == INT4:
+            out[:, :, i] = np.where(f >= 8, f.astype(np.int64) - 16, f.astype(np.int64)).astype(np.int8)
+        elif bits == TERNARY:
             out[:, :, i] = (f & 1).astype(np.int8) - ((f >> 1) & 1).astype(np.int8)
         else:
             out[:, :, i] = 2 * f.astype(np.int8) - 1

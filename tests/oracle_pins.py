@@ -414,3 +414,52 @@ def pin_import_layouts_agree(o, seed=43):
 
 
 IMPORT_PINS = [pin_import_golden, pin_import_other_routes, pin_import_layouts_agree]
+
+
+# ----------------------------------------------------------------------------------------
+# 4-bit codes (two's complement nibbles, 8 per word, least significant first)
+
+def pin_int4_hex_words(o, seed=51):
+    """4-bit words equal integers parsed from hex strings written most-significant nibble first
+    (the digit of c is "0123456789ABCDEF"[c mod 16], looked up, not computed by the packer's
+    rule), and unpacking returns every one of the 16 codes."""
+    digits = "0123456789ABCDEF"
+    rng = np.random.default_rng(seed)
+    codes = gen_codes(rng, 6, 64, 4)
+    codes[0, :16] = np.arange(-8, 8)
+    w, bad = o.pack(codes, 4)
+    assert bad == 0 and w.shape == (6, 8)
+    for n in range(6):
+        for j in range(8):
+            chunk = codes[n, 8 * j:8 * j + 8]
+            expect = int("".join(digits[int(c) + 16 if c < 0 else int(c)] for c in reversed(chunk)), 16)
+            assert int(w[n, j]) == expect, (n, j)
+    assert np.array_equal(o.unpack(w, 64, 4), codes)
+    # outside [-8, 7]: packed as 0 and counted
+    w, bad = o.pack(np.array([[8, -9, 100, 1, 0, 0, 0, 0]], dtype=np.int8), 4)
+    assert bad == 3 and int(w[0, 0]) == 0x00001000
+
+
+def pin_int4_one_hot(o):
+    """One nonzero 4-bit code c at (n0, k0): Y[:, n0] = c * S[n0, grp] * X[:, k0] exactly (an
+    exact fp64 product), every other column 0; the extreme codes -8 and 7 included."""
+    rng = rng_for(7, 98, 0)
+    M, N, K, g = 3, 16, 128, 64
+    x = gen_x(rng, M, K)
+    s = gen_scales(rng, N, K, g)
+    xf = o.bf16_bits_to_f64(x)
+    for (n0, k0, grp, c0) in ((0, 0, 0, -8), (15, 127, 1, 7), (5, 64, 1, -1), (9, 63, 0, 3)):
+        c = np.zeros((N, K), dtype=np.int8)
+        c[n0, k0] = c0
+        w, _ = o.pack(c, 4)
+        y = o.gemm_ref_f64(x, o.unpack(w, K, 4), s, g)
+        assert np.array_equal(y[:, n0], c0 * float(s[n0, grp]) * xf[:, k0]), (n0, k0)
+        assert not np.any(np.delete(y, n0, axis=1))
+
+
+def pin_int4_fsum(o):
+    """The 4-bit GEMM against math.fsum of exact products (codes up to magnitude 8)."""
+    pin_fsum(o, M=16, N=48, K=256, g=64, bits=4, seed=9)
+
+
+INT4_PINS = [pin_int4_hex_words, pin_int4_one_hot, pin_int4_fsum]

@@ -140,6 +140,27 @@ def test_import_rejects_before_touching_the_device():
     assert L.lowbit_import_ternary(0, GL, 1, 0, 0, 256, None, None) == OK                       # empty
 
 
+def test_int4_arguments_and_kernel():
+    """4-bit codes: g = 64 / 128 on the 16x16-block tile kernel at every M (forced variants of
+    other kernels included); g = 32 and other bit widths are refused."""
+    L = _lib.lib()
+    assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 64, 4) == OK
+    assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 128, 4) == OK
+    assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 32, 4) == UNSUPPORTED
+    assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 64, 3) == UNSUPPORTED
+    assert L.lowbit_pack(A, A, 16, 12, 4, None, None) == INVALID          # K % 8
+    assert L.lowbit_pack(A, A, 16, 24, 3, None, None) == UNSUPPORTED
+    tile16 = {"tile288x192", "tile96x192", "tile96x192k2"}
+    for M, N, K in ((1, 16, 64), (16, 3072, 2560), (512, 19456, 2560), (512, 2560, 9728), (4608, 3072, 3072)):
+        assert lb.variant(M, N, K, 64, 4) in tile16, (M, N, K)
+
+
+def test_int4_forced_variants_stay_on_the_tile16_kernel(monkeypatch):
+    for v in ("skinny", "resident", "tile64", "tile256w"):
+        monkeypatch.setenv("LOWBIT_VARIANT", v)
+        assert lb.variant(16, 3072, 2560, 64, 4) in {"tile288x192", "tile96x192", "tile96x192k2"}, v
+
+
 def test_variant_choice():
     """Tile choice: fewest rounds of tiles over 256 compute units, weighted by tile work.
     4608 x 3072 is 216 tiles of 256 x 256 (40 units idle) but exactly 256 of 288 x 192."""

@@ -10,7 +10,7 @@ from oracle import lowbit_ref as ref
 from tests import oracle_pins as P
 
 
-@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS + P.IMPORT_PINS,
+@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS + P.IMPORT_PINS + P.INT4_PINS,
                          ids=lambda f: f.__name__)
 def test_pin_holds(pin):
     pin(P.real_oracle())
@@ -328,3 +328,43 @@ def test_import_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError):
             failures.append(pin.__name__)
     assert failures, f"planted mistake {name} passed every import pin"
+
+
+# planted 4-bit mistakes: an unsigned nibble decode, most-significant nibble first (in pack and
+# unpack alike), and a scale applied to the wrong group of a 4-bit weight
+
+
+def _int4_unsigned_unpack(words, K, bits):
+    out = oracle.unpack(words, K, bits)
+    return (out.astype(np.int64) % 16).astype(np.int8) if bits == 4 else out
+
+
+def _int4_msb_pack(codes, bits):
+    if bits != 4:
+        return oracle.pack(codes, bits)
+    c = np.asarray(codes, dtype=np.int8)
+    w, bad = oracle.pack(c.reshape(c.shape[0], -1, 8)[:, :, ::-1].reshape(c.shape), 4)
+    return w, bad
+
+
+def _int4_msb_unpack(words, K, bits):
+    out = oracle.unpack(words, K, bits)
+    return out.reshape(out.shape[0], -1, 8)[:, :, ::-1].reshape(out.shape) if bits == 4 else out
+
+
+INT4_PLANTED = {
+    "unsigned_nibbles": dict(unpack=_int4_unsigned_unpack),
+    "msb_first_nibbles": dict(pack=_int4_msb_pack, unpack=_int4_msb_unpack),
+}
+
+
+@pytest.mark.parametrize("name", sorted(INT4_PLANTED))
+def test_int4_planted_mistake_is_caught(name):
+    broken = SimpleNamespace(**{**vars(P.real_oracle()), **INT4_PLANTED[name]})
+    failures = []
+    for pin in P.INT4_PINS + [P.pin_golden_words]:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every 4-bit pin"

@@ -31,6 +31,7 @@ import numpy as np
 
 TERNARY = 2
 BINARY = 1
+INT4 = 4
 
 
 def rng_for(seed: int, config_id: int, tensor_id: int) -> np.random.Generator:
@@ -54,14 +55,17 @@ _TERNARY_FROM_2BITS = np.array([-1, 0, 0, 1], dtype=np.int8)
 
 
 def gen_codes(rng: np.random.Generator, N: int, K: int, bits: int) -> np.ndarray:
-    """int8 codes, shape [N, K]: ternary P(-1)=P(+1)=1/4, P(0)=1/2; binary P(+-1)=1/2."""
+    """int8 codes, shape [N, K]: ternary P(-1)=P(+1)=1/4, P(0)=1/2; binary P(+-1)=1/2;
+    4-bit uniform on the integers -8 .. 7."""
     if bits == TERNARY:
         u = rng.integers(0, 4, size=(N, K), dtype=np.uint8)
         return _TERNARY_FROM_2BITS[u]
     if bits == BINARY:
         u = rng.integers(0, 2, size=(N, K), dtype=np.int8)
         return (u * np.int8(2) - np.int8(1)).astype(np.int8)
-    raise ValueError(f"bits must be 1 or 2, got {bits}")
+    if bits == INT4:
+        return rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+    raise ValueError(f"bits must be 1, 2 or 4, got {bits}")
 
 
 def gen_scales(rng: np.random.Generator, N: int, K: int, g: int) -> np.ndarray:
