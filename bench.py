@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 VARIANT_SOURCES = {
     "tile256x256": ["gemm_tiled.hip"], "tile256x128": ["gemm_tiled.hip"], "tile128x256": ["gemm_tiled.hip"],
     "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "tile96x192": ["gemm_tile16.hip"],
-    "tile96x192k2": ["gemm_tile16.hip"],
+    "tile96x192k2": ["gemm_tile16.hip"], "tile64x128k2": ["gemm_tile16.hip"],
     "skinny": ["gemm_skinny.hip"],
     "resident": ["gemm_resident.hip"],
 }

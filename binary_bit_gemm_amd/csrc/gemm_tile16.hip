@@ -504,6 +504,15 @@ hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hi
     // 96 x 192 in 4 waves of 96 x 48 (LDS 60 KB): 1536 x 3072 outputs are exactly 256 tiles.
     // With K split between two groups of 4 waves (LDS 120 KB) where every problem has an even
     // number of 64-element steps.
+    if constexpr (BITS == 4) {
+        // 64 x 128 in two groups of 4 waves of 64 x 32 (LDS 80 KB), K split between the groups
+        if (variant == TILE_64x128K2) {
+            bool even = true;
+            for (int i = 0; i < count; ++i) even = even && (probs[i].K / KS) % 2 == 0;
+            if (even) return launch_cfg16<G, BITS, 64, 128, 1, 4, 2>(probs, count, stream);
+            return launch_cfg16<G, BITS, 64, 128, 1, 4>(probs, count, stream);
+        }
+    }
     if (variant == TILE_96x192K2) {
         bool even = true;
         for (int i = 0; i < count; ++i) even = even && (probs[i].K / KS) % 2 == 0;

@@ -384,6 +384,9 @@ constexpr TileShape kTiles[] = {
     {TILE_64x256, 64, 256, 2, 0.75f, 0.75f},
     {TILE_96x192, 96, 192, 1, 0.54f, 0.51f},
     {TILE_96x192K2, 96, 192, 1, 0.65f, 0.62f},
+    // 4-bit codes only (the one kernel they run on): fills the chip where 96 x 192 leaves most
+    // compute units idle, e.g. the text encoder's 512 x 2560 down projection (160 vs 84 tiles)
+    {TILE_64x128K2, 64, 128, 1, 0.40f, 0.40f},
 };
 
 }  // namespace
@@ -394,6 +397,11 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
     for (const TileShape& t : kTiles) {
         if (is_tile16_variant(t.variant) && !tile16_supported(g, bits)) continue;
         if (bits == 4 && !is_tile16_variant(t.variant)) continue;  // 4-bit codes: the 16x16-block tile only
+        if (t.variant == TILE_64x128K2) {
+            bool skip = bits != 4;
+            for (int i = 0; i < count; ++i) skip = skip || (probs[i].K / 64) % 2 != 0;
+            if (skip) continue;
+        }
         if ((t.variant == TILE_96x192 || t.variant == TILE_96x192K2) && bits != 4) {
             // measured at M = 1536; below M = 1024 they stay unused.  The K split needs an even
             // number of 64-element steps.
@@ -430,6 +438,7 @@ const char* tile_variant_name(int variant) {
         case TILE_288x192: return "tile288x192";
         case TILE_96x192: return "tile96x192";
         case TILE_96x192K2: return "tile96x192k2";
+        case TILE_64x128K2: return "tile64x128k2";
         default: return "tile64x256";
     }
 }

@@ -69,6 +69,7 @@ int forced_variant() {
     if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
     if (std::strcmp(v, "tile96") == 0) return lowbit::TILE_96x192;
     if (std::strcmp(v, "tile96k2") == 0) return lowbit::TILE_96x192K2;
+    if (std::strcmp(v, "tile64k2") == 0) return lowbit::TILE_64x128K2;
     if (std::strcmp(v, "resident") == 0) return 102;
     return -1;
 }

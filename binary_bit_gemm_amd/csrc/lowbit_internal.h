@@ -47,9 +47,12 @@ hipError_t launch_import(const void* src, int layout, int zero, uint32_t* W, int
 // TILE_288x192 and TILE_96x192 are the 16x16x32-block kernel (g = 64 or 128 only).
 enum TileVariant {
     TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5,
-    TILE_96x192K2 = 6  // 96 x 192 with K split between two groups of 4 waves (even step counts)
+    TILE_96x192K2 = 6,  // 96 x 192 with K split between two groups of 4 waves (even step counts)
+    TILE_64x128K2 = 7   // 64 x 128, the same K split (4-bit codes: small output grids)
 };
-inline bool is_tile16_variant(int v) { return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2; }
+inline bool is_tile16_variant(int v) {
+    return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2 || v == TILE_64x128K2;
+}
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.

@@ -150,7 +150,7 @@ def test_int4_arguments_and_kernel():
     assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 64, 3) == UNSUPPORTED
     assert L.lowbit_pack(A, A, 16, 12, 4, None, None) == INVALID          # K % 8
     assert L.lowbit_pack(A, A, 16, 24, 3, None, None) == UNSUPPORTED
-    tile16 = {"tile288x192", "tile96x192", "tile96x192k2"}
+    tile16 = {"tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"}
     for M, N, K in ((1, 16, 64), (16, 3072, 2560), (512, 19456, 2560), (512, 2560, 9728), (4608, 3072, 3072)):
         assert lb.variant(M, N, K, 64, 4) in tile16, (M, N, K)
 
@@ -158,7 +158,7 @@ def test_int4_arguments_and_kernel():
 def test_int4_forced_variants_stay_on_the_tile16_kernel(monkeypatch):
     for v in ("skinny", "resident", "tile64", "tile256w"):
         monkeypatch.setenv("LOWBIT_VARIANT", v)
-        assert lb.variant(16, 3072, 2560, 64, 4) in {"tile288x192", "tile96x192", "tile96x192k2"}, v
+        assert lb.variant(16, 3072, 2560, 64, 4) in {"tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"}, v
 
 
 def test_variant_choice():

@@ -61,13 +61,13 @@ def test_int4_gemm_parity(M, N, K, g):
     _check(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"int4 {M}x{N}x{K} g{g}")
 
 
-@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2"])
+@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2", "tile64k2"])
 @pytest.mark.parametrize("g", [64, 128])
 def test_int4_every_tile_variant(variant, g, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
     M, N, K = 200, 400, 1536  # 24 steps: even, so tile96k2 splits K
     assert lb.variant(M, N, K, g, 4) == {"tile288": "tile288x192", "tile96": "tile96x192",
-                                         "tile96k2": "tile96x192k2"}[variant]
+                                         "tile96k2": "tile96x192k2", "tile64k2": "tile64x128k2"}[variant]
     inp = _inputs(M, N, K, g, seed=3)
     y, _ = run_gemm(inp, g, 4)
     _check(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"int4 {variant} g{g}")
