@@ -134,3 +134,28 @@ def test_swiglu_rejects_g32_and_odd_rows():
         lb.gemm_swiglu(x, w, s, 32, 2)
     with pytest.raises(ValueError):
         lb.gemm_swiglu(x, w[:31], s[:31, :1], 64, 2)
+
+
+def test_swiglu_on_the_fused_single_stream_linear():
+    """The single-stream 3072 -> 27648 linear holds [QKV 9216 | gate 9216 | up 9216] rows; its
+    MLP part takes the fused SwiGLU and its QKV part the plain GEMM, as two calls on row slices of
+    the one packed weight (offset pointers into the same buffers, no copy); sampled columns
+    against the oracle."""
+    t = torch()
+    M, K, g, bits, H = 96, 3072, 64, 2, 9216
+    p = W.Problem("single_fused", M, 3 * H, K, bits, g, 90, 77)
+    inp = W.make_inputs(p, 0)
+    x = dev_x(inp.x)
+    words, bad = lb.pack(dev_codes(inp.codes), bits)
+    assert bad == 0
+    s = dev_scales(inp.scales)
+    qkv = host_bits(lb.gemm(x, words[:H], s[:H], g, bits))
+    mlp = host_bits(lb.gemm_swiglu(x, words[H:], s[H:], g, bits))
+    t.cuda.synchronize()
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(H - 8, H), np.random.default_rng(4).choice(H, 48, replace=False)]))
+    r = oracle.check_tolerance(qkv[:, cols], oracle.gemm_ref_f64(inp.x, inp.codes[cols], inp.scales[cols], g))
+    assert r["ok"], r
+    rows = np.concatenate([H + cols, 2 * H + cols])
+    ref = oracle.swiglu_ref_f64(inp.x, inp.codes[rows], inp.scales[rows], g)
+    r = oracle.check_tolerance(mlp[:, cols], ref)
+    assert r["ok"], r
