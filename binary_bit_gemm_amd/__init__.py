@@ -125,6 +125,20 @@ def import_mlx(src, N: int, K: int, zero: int = 1, count_invalid: bool = True):
     return _import(src, LAYOUT_MLX_U32, N, K, zero, count_invalid)
 
 
+def import_gemlite_binary(src, N: int, K: int):
+    """GemLite 1-bit weights, uint8 [K/8, N] (transposed, bit i of byte (j, n) = code 8j + i,
+    1 -> +1) -> packed binary words [N, K/32] as int32."""
+    torch = _torch()
+    _require(src, torch.uint8, "src")
+    if tuple(src.shape) != (K // 8, N) or K % 8:
+        raise ValueError(f"GemLite 1-bit src must be uint8 [K/8, N] = ({K // 8}, {N}), got {tuple(src.shape)}")
+    words = torch.empty((N, words_per_row(K, 1)), dtype=torch.int32, device=src.device)
+    st = lib().lowbit_import_binary_gemlite(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(words.data_ptr()), N, K,
+                                            ctypes.c_void_p(_stream_ptr(src.device)))
+    _check(st, "lowbit_import_binary_gemlite")
+    return words
+
+
 def workspace_size(M: int, N: int, K: int, g: int = 64, bits: int = 2) -> int:
     """Bytes of workspace lowbit_gemm_ex can use for this shape (0: none needed)."""
     return int(lib().lowbit_workspace_size(M, N, K, g, bits))

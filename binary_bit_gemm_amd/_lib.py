@@ -14,6 +14,7 @@ SIGNATURES = {
     "lowbit_pack": (_INT, [_VP, _VP, _I64, _I64, _INT, _VP, _VP]),
     "lowbit_unpack": (_INT, [_VP, _VP, _I64, _I64, _INT, _VP]),
     "lowbit_import_ternary": (_INT, [_VP, _INT, _INT, _VP, _I64, _I64, _VP, _VP]),
+    "lowbit_import_binary_gemlite": (_INT, [_VP, _VP, _I64, _I64, _VP]),
     "lowbit_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "lowbit_gemm_batched": (_INT, [_VP, _INT, _VP]),
     "lowbit_gemm_swiglu": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),

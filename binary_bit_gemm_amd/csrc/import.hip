@@ -9,6 +9,9 @@
 //   MLX (uint32, row-major by output): src[N][K/16]; word (n, j) holds codes k = 16j .. 16j+15
 //     ("backend/ -- FastAPI Mac backend", section "Checkpoint layout": uint32 packed weights).
 // Codes outside {-1, 0, +1} pack as the 0 field and are counted, as in lowbit_pack.
+// Binary weights (the binary model card's GemLite 1-bit format) take the same transposed byte
+// layout with 8 codes per byte, src[K/8][N], bit i of byte (j, n) holding code 8j + i (bit 1 ->
+// +1): the bytes of a word are then already this library's bits, and only the transpose remains.
 #include "lowbit_internal.h"
 
 namespace lowbit {
@@ -57,13 +60,14 @@ constexpr int kTileN = 64;      // output rows (source columns) per workgroup
 constexpr int kTileJ = 16;      // output words per row per workgroup
 constexpr int kTileR = 4 * kTileJ;  // source rows per workgroup
 
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void import_gemlite_kernel(const uint8_t* __restrict__ src,
                                                                   uint32_t* __restrict__ W, int64_t N,
                                                                   int64_t K, int zero,
                                                                   int32_t* __restrict__ bad_count) {
     // [source row][4 columns per dword]; one padding dword per row
     __shared__ uint32_t tile[kTileR][kTileN / 4 + 1];
-    const int64_t rows = K / 4, wpr = K / 16;
+    const int64_t rows = K * BITS / 8, wpr = K * BITS / 32;
     const int64_t n0 = int64_t(blockIdx.x) * kTileN;
     const int64_t r0 = int64_t(blockIdx.y) * kTileR;
     const int t = threadIdx.x;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void import_gemlite_kernel(const uint8_t*
             uint32_t levels = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) levels |= ((tile[4 * j + i][n / 4] >> (8 * (n % 4))) & 0xFFu) << (8 * i);
-            W[gn * wpr + gj] = remap_word(levels, zero, bad);
+            W[gn * wpr + gj] = BITS == 2 ? remap_word(levels, zero, bad) : levels;
         }
     }
     add_bad(bad, bad_count);
@@ -110,9 +114,17 @@ hipError_t launch_import(const void* src, int layout, int zero, uint32_t* W, int
                            nwords, zero, bad_count);
     } else {
         const dim3 grid(unsigned((N + kTileN - 1) / kTileN), unsigned((K / 16 + kTileJ - 1) / kTileJ));
-        hipLaunchKernelGGL(import_gemlite_kernel, grid, dim3(kThreads), 0, stream, static_cast<const uint8_t*>(src), W,
-                           N, K, zero, bad_count);
+        hipLaunchKernelGGL(import_gemlite_kernel<2>, grid, dim3(kThreads), 0, stream, static_cast<const uint8_t*>(src),
+                           W, N, K, zero, bad_count);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t N, int64_t K, hipStream_t stream) {
+    if (N * K == 0) return hipSuccess;
+    const dim3 grid(unsigned((N + kTileN - 1) / kTileN), unsigned((K / 32 + kTileJ - 1) / kTileJ));
+    hipLaunchKernelGGL(import_gemlite_kernel<1>, grid, dim3(kThreads), 0, stream, src, W, N, K, 0,
+                       static_cast<int32_t*>(nullptr));
     return hipGetLastError();
 }
 

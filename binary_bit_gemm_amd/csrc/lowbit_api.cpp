@@ -264,6 +264,18 @@ int lowbit_import_ternary(const void* src, int layout, int zero, uint32_t* W, in
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 
+int lowbit_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t N, int64_t K, void* stream) {
+    if (N < 0 || K < 0 || N % 16 != 0 || K % 32 != 0) return LOWBIT_E_INVALID;
+    if (N > kMaxDim || K > kMaxK || N * K > kMaxCodes) return LOWBIT_E_UNSUPPORTED;
+    if (N * K == 0) return LOWBIT_OK;
+    if (src == nullptr || W == nullptr) return LOWBIT_E_INVALID;
+    if (!aligned16(src) || !aligned16(W)) return LOWBIT_E_ALIGN;
+    int st = device_check();
+    if (st != LOWBIT_OK) return st;
+    hipError_t e = lowbit::launch_import_binary_gemlite(src, W, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
 int lowbit_gemm(const void* X, const uint32_t* W, const void* S, void* Y,
                 int64_t M, int64_t N, int64_t K, int g, int bits, void* stream) {
     int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);

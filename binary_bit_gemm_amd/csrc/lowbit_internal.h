@@ -42,6 +42,7 @@ constexpr int kLayoutGemliteU8T = 1;
 constexpr int kLayoutMlxU32 = 2;
 hipError_t launch_import(const void* src, int layout, int zero, uint32_t* W, int64_t N, int64_t K,
                          int32_t* bad_count, hipStream_t stream);
+hipError_t launch_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t N, int64_t K, hipStream_t stream);
 
 // Tiled MFMA kernels (LDS-staged X, packed weights and scales).  `variant` selects the tile;
 // TILE_288x192 and TILE_96x192 are the 16x16x32-block kernel (g = 64 or 128 only).

@@ -118,6 +118,21 @@ int lowbit_import_ternary(const void* src, int layout, int zero, uint32_t* W, in
                           int32_t* bad_count, void* stream);
 
 /*
+ * lowbit_import_binary_gemlite -- binary weights in GemLite's transposed 1-bit pack -> packed
+ * words [N, K/32] in the format above (offline, like lowbit_pack).
+ *   src  device uint8 [K/8, N]: bit i of byte (j, n) is code k = 8j + i of output row n, 1 -> +1,
+ *        0 -> -1.  The binary model card ("bonsai-image-binary-4B-gemlite-1bit", "Binary Weight
+ *        Representation: 1-bit g128") gives w = scale_g * b with b in {-1, +1} and a GemLite
+ *        1-bit pack; the byte orientation is the one the Bonsai-Image-Demo pull request's "CPU
+ *        bring-up" comment gives for GemLite's int2 weights, (in_features / bytes-per-code,
+ *        out_features).  Every bit pattern is a valid code.
+ *   W    device, N*K/32 uint32, written.
+ *   Requires N % 16 == 0, K % 32 == 0, K <= 2^22, 16-byte aligned src and W.  Scales are the
+ *   caller's (the card's per-group fp16 scale_g is the library's scale).
+ */
+int lowbit_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t N, int64_t K, void* stream);
+
+/*
  * lowbit_gemm -- Y[M, N] = X[M, K] . dequant(W)[N, K]^T, bf16 out (round to nearest even).
  *   X  device bf16 [M, K];  W  device packed words [N, K*bits/32];
  *   S  device fp16 [N, K/g];  Y  device bf16 [M, N], fully overwritten.

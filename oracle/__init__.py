@@ -35,5 +35,6 @@ from .lowbit_ref import (  # noqa: F401
     pack, unpack, dequant_f64, gemm_ref_f64, gemm_ref_from_words, gemm_fsum_element,
     silu_f64, swiglu_ref_f64, residual_ref_f64,
     gemlite_u8t_decode, gemlite_u8t_encode, mlx_u32_decode, mlx_u32_encode,
+    gemlite_binary_decode, gemlite_binary_encode,
     check_tolerance, REL_FROB_TOL, ELEM_TOL,
 )

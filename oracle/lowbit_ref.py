@@ -183,6 +183,30 @@ def mlx_u32_decode(src: np.ndarray, N: int, K: int, zero: int = 1) -> Tuple[np.n
     return _level_codes(q, zero)
 
 
+def gemlite_binary_decode(src: np.ndarray, N: int, K: int) -> np.ndarray:
+    """GemLite 1-bit transposed uint8 [K/8, N] -> binary codes [N, K]: code k of row n is
+    2 * (bit k % 8 of byte (k // 8, n)) - 1 (reading R8 with 8 codes per byte)."""
+    b = np.asarray(src, dtype=np.uint8)
+    if b.shape != (K // 8, N) or K % 8:
+        raise ValueError("GemLite 1-bit src must be [K/8, N]")
+    out = np.zeros((N, K), dtype=np.int8)
+    for k in range(K):
+        out[:, k] = 2 * ((b[k // 8, :] >> (k % 8)) & 1).astype(np.int8) - 1
+    return out
+
+
+def gemlite_binary_encode(codes: np.ndarray) -> np.ndarray:
+    """Binary codes [N, K] (+1 / -1) -> GemLite 1-bit transposed uint8 [K/8, N]."""
+    c = np.asarray(codes, dtype=np.int8)
+    N, K = c.shape
+    if K % 8 or np.any((c != 1) & (c != -1)):
+        raise ValueError("binary codes and K a multiple of 8")
+    out = np.zeros((K // 8, N), dtype=np.uint8)
+    for k in range(K):
+        out[k // 8, :] |= ((c[:, k] == 1).astype(np.uint8) << (k % 8)).astype(np.uint8)
+    return out
+
+
 def gemlite_u8t_encode(codes: np.ndarray, zero: int = 1) -> np.ndarray:
     """int8 codes [N, K] -> GemLite transposed uint8 [K/4, N] with levels q = c + zero (0..3)."""
     c = np.asarray(codes, dtype=np.int64)

@@ -39,7 +39,9 @@ def real_oracle():
                            bf16_bits_to_f64=oracle.bf16_bits_to_f64, silu_f64=oracle.silu_f64,
                            swiglu_ref_f64=oracle.swiglu_ref_f64, residual_ref_f64=oracle.residual_ref_f64,
                            gemlite_u8t_decode=oracle.gemlite_u8t_decode, gemlite_u8t_encode=oracle.gemlite_u8t_encode,
-                           mlx_u32_decode=oracle.mlx_u32_decode, mlx_u32_encode=oracle.mlx_u32_encode)
+                           mlx_u32_decode=oracle.mlx_u32_decode, mlx_u32_encode=oracle.mlx_u32_encode,
+                           gemlite_binary_decode=oracle.gemlite_binary_decode,
+                           gemlite_binary_encode=oracle.gemlite_binary_encode)
 
 
 # ----------------------------------------------------------------------------------------
@@ -413,7 +415,38 @@ def pin_import_layouts_agree(o, seed=43):
         assert ba == bm == 0 and np.array_equal(a, codes) and np.array_equal(m, codes)
 
 
-IMPORT_PINS = [pin_import_golden, pin_import_other_routes, pin_import_layouts_agree]
+def pin_import_binary(o, seed=45):
+    """GemLite 1-bit bytes: hand-worked values (all +1 -> 0xFF, all -1 -> 0x00, code (2, 5) = +1
+    among -1 -> byte (0, 2) = 0x20; a square buffer, K/8 = N = 16, with code (0, 127) = +1 in
+    byte (15, 0) = 0x80), and random codes through numpy's little-endian unpackbits and a
+    transpose, then through the library's own binary words."""
+    z = -np.ones((16, 16), dtype=np.int8)
+    assert np.all(o.gemlite_binary_encode(-z) == 0xFF) and np.all(o.gemlite_binary_encode(z) == 0x00)
+    one = z.copy()
+    one[2, 5] = 1
+    b = o.gemlite_binary_encode(one)
+    assert b.shape == (2, 16) and b[0, 2] == 0x20 and np.count_nonzero(b) == 1
+    assert np.array_equal(o.gemlite_binary_decode(b, 16, 16), one)
+    sq = np.zeros((16, 16), dtype=np.uint8)
+    sq[15, 0] = 0x80
+    codes = o.gemlite_binary_decode(sq, 16, 128)
+    assert codes[0, 127] == 1 and np.count_nonzero(codes == 1) == 1
+    rng = np.random.default_rng(seed)
+    N, K = 32, 256
+    codes = gen_codes(rng, N, K, 1)
+    b = o.gemlite_binary_encode(codes)
+    bits = np.unpackbits(b[:, :, None], axis=2, bitorder="little")         # [K/8, N, 8]
+    direct = 2 * bits.transpose(0, 2, 1).reshape(K, N).T.astype(np.int8) - 1
+    assert np.array_equal(direct, codes)
+    got = o.gemlite_binary_decode(b, N, K)
+    assert np.array_equal(got, codes)
+    w, bad = o.pack(got, 1)
+    assert bad == 0
+    # word j of row n is bytes 4j .. 4j+3 of column n, little-endian
+    assert np.array_equal(w, np.ascontiguousarray(b.T).view("<u4"))
+
+
+IMPORT_PINS = [pin_import_golden, pin_import_other_routes, pin_import_layouts_agree, pin_import_binary]
 
 
 # ----------------------------------------------------------------------------------------

@@ -138,6 +138,11 @@ def test_import_rejects_before_touching_the_device():
     assert L.lowbit_import_ternary(A + 4, GL, 1, A, 64, 256, None, None) == ALIGN
     assert L.lowbit_import_ternary(A, MLX, 1, A + 8, 64, 256, None, None) == ALIGN
     assert L.lowbit_import_ternary(0, GL, 1, 0, 0, 256, None, None) == OK                       # empty
+    assert L.lowbit_import_binary_gemlite(A, A, 40, 256, None) == INVALID                        # N % 16
+    assert L.lowbit_import_binary_gemlite(A, A, 64, 48, None) == INVALID                         # K % 32
+    assert L.lowbit_import_binary_gemlite(A + 4, A, 64, 256, None) == ALIGN
+    assert L.lowbit_import_binary_gemlite(A, A, 16, (1 << 22) + 32, None) == UNSUPPORTED
+    assert L.lowbit_import_binary_gemlite(0, 0, 0, 256, None) == OK
 
 
 def test_int4_arguments_and_kernel():

@@ -1,6 +1,6 @@
-"""GPU parity of the ternary importers (lowbit_import_ternary: GemLite transposed uint8 and
-MLX uint32 rows -> the library's words) against the oracle, through the C-ABI: bit-exact words
-and the same count of invalid levels."""
+"""GPU parity of the importers (lowbit_import_ternary: GemLite transposed uint8 and MLX uint32
+rows; lowbit_import_binary_gemlite: GemLite's transposed 1-bit bytes) against the oracle, through
+the C-ABI: bit-exact words and the same count of invalid levels."""
 from __future__ import annotations
 
 import numpy as np
@@ -95,3 +95,25 @@ def test_import_shape_is_checked_not_guessed():
         lb.import_gemlite(src, 768, 12288)                         # the direct reading's shape
     words, bad = lb.import_gemlite(src, 3072, 3072, zero=0)        # level 0 at zero 0: code 0
     assert bad == 0 and words.shape == (3072, 192) and not t.any(words).item()
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (208, 1056), (16, 32), (3072, 3072), (9216, 3072)])
+def test_import_gemlite_binary(N, K):
+    """GemLite 1-bit bytes [K/8, N] -> binary words, bit-exact against the oracle's decode and
+    pack (random bytes: every pattern is a code), on one tile, ragged tiles (N % 64 == 16, 33
+    words a row), the smallest shape, a square weight and the 3072 -> 9216 linear."""
+    rng = np.random.default_rng(N + 3 * K)
+    src = rng.integers(0, 256, size=(K // 8, N), dtype=np.uint8)
+    got = host_words(lb.import_gemlite_binary(torch().from_numpy(src).cuda(), N, K))
+    want, bad = oracle.pack(oracle.gemlite_binary_decode(src, N, K), 1)
+    assert bad == 0 and np.array_equal(got, want)
+
+
+def test_imported_binary_weight_runs_the_gemm():
+    """The binary card's format end to end: GemLite 1-bit bytes, g = 128, through lowbit_gemm."""
+    M, N, K, g = 64, 3072, 3072, 128
+    inp = W.make_inputs(W.Problem("import_b", M, N, K, 1, g, 92, 6), 0)
+    words = lb.import_gemlite_binary(torch().from_numpy(oracle.gemlite_binary_encode(inp.codes)).cuda(), N, K)
+    y = host_bits(lb.gemm(dev_x(inp.x), words, dev_scales(inp.scales), g, 1))
+    r = oracle.check_tolerance(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g))
+    assert r["ok"], r

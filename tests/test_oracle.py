@@ -310,7 +310,37 @@ def _mlx_word_order_encode(codes, zero=1):
     return np.ascontiguousarray(oracle.mlx_u32_encode(codes, zero)[:, ::-1])
 
 
+def _glb_msb_decode(src, N, K):
+    b = np.asarray(src, dtype=np.uint8)
+    return np.stack([2 * ((b[k // 8, :] >> (7 - k % 8)) & 1).astype(np.int8) - 1 for k in range(K)], axis=1)
+
+
+def _glb_msb_encode(codes):
+    c = np.asarray(codes, dtype=np.int8)
+    out = np.zeros((c.shape[1] // 8, c.shape[0]), dtype=np.uint8)
+    for k in range(c.shape[1]):
+        out[k // 8, :] |= ((c[:, k] == 1).astype(np.uint8) << (7 - k % 8)).astype(np.uint8)
+    return out
+
+
+def _glb_direct_decode(src, N, K):
+    b = np.asarray(src, dtype=np.uint8).reshape(N, K // 8)  # the orientation trap
+    return np.stack([2 * ((b[:, k // 8] >> (k % 8)) & 1).astype(np.int8) - 1 for k in range(K)], axis=1)
+
+
+def _glb_direct_encode(codes):
+    c = np.asarray(codes, dtype=np.int8)
+    N, K = c.shape
+    out = np.zeros((N, K // 8), dtype=np.uint8)
+    for k in range(K):
+        out[:, k // 8] |= ((c[:, k] == 1).astype(np.uint8) << (k % 8)).astype(np.uint8)
+    return out.reshape(K // 8, N)
+
+
 IMPORT_PLANTED = {
+    "gemlite_binary_msb_first": dict(gemlite_binary_decode=_glb_msb_decode, gemlite_binary_encode=_glb_msb_encode),
+    "gemlite_binary_direct_orientation": dict(gemlite_binary_decode=_glb_direct_decode,
+                                              gemlite_binary_encode=_glb_direct_encode),
     "gemlite_msb_first": dict(gemlite_u8t_decode=_gl_msb_decode, gemlite_u8t_encode=_gl_msb_encode),
     "gemlite_direct_orientation": dict(gemlite_u8t_decode=_gl_direct_decode, gemlite_u8t_encode=_gl_direct_encode),
     "mlx_code_sign": dict(mlx_u32_decode=_mlx_sign_decode, mlx_u32_encode=_mlx_sign_encode),
