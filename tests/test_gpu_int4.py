@@ -138,3 +138,20 @@ def test_int4_in_a_batched_call_with_ternary():
     lb.gemm_batched(probs)
     for out, inp, g in outs:
         _check(host_bits(out), oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), "batched")
+
+
+def test_int4_empty_and_k0():
+    """M = 0 is a no-op, K = 0 gives Y = 0 (every output overwritten), N = 0 packs nothing."""
+    t = torch()
+    x0 = t.zeros((5, 0), dtype=t.bfloat16, device="cuda")
+    w0 = t.zeros((32, 0), dtype=t.int32, device="cuda")
+    s0 = t.zeros((32, 0), dtype=t.float16, device="cuda")
+    y = t.full((5, 32), 3.0, dtype=t.bfloat16, device="cuda")
+    lb.gemm(x0, w0, s0, 64, 4, out=y)
+    assert not y.float().abs().sum().item()
+    x = t.zeros((0, 64), dtype=t.bfloat16, device="cuda")
+    w = t.zeros((32, 8), dtype=t.int32, device="cuda")
+    s = t.ones((32, 1), dtype=t.float16, device="cuda")
+    assert lb.gemm(x, w, s, 64, 4).shape == (0, 32)
+    words, bad = lb.pack(t.zeros((0, 64), dtype=t.int8, device="cuda"), 4)
+    assert words.shape == (0, 8) and bad == 0
