@@ -179,11 +179,8 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=Fal
     import numpy as np
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    host = host_info()
+    threads = host["blas_threads"]
     seen = {}
     for p in probs:
         seen.setdefault((p.N, p.K, p.bits, p.g), p)
@@ -212,7 +209,39 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=Fal
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": (f"all {probs[0].M}" if rows <= 0 else f"first {rows}") +
                       f" rows of X for each of the {len(seen)} distinct (N, K) shapes, {passes} passes; "
-                      f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s"}
+                      f"numpy unpack + fp64 dequantise + fp64 matmul; {elapsed:.1f} s",
+            "host": host}
+
+
+def host_info():
+    """The host the CPU baseline runs on: CPU model, logical CPUs the OS reports, CPUs this
+    process may run on (affinity), and the BLAS library numpy calls with its thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = None
+    blas, threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            d = libs[0]
+            blas = f"{d.get('internal_api')} {d.get('version')}"
+            threads = d.get("num_threads")
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas,
+            "blas_threads": threads or affinity or os.cpu_count() or 1,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def main():

@@ -43,6 +43,14 @@ constexpr int kTargetWorkgroups = 256;  // whole-K plans: one per compute unit
 // on the M = 16 K-heavy shapes: 4..8 column blocks and 384..768 workgroups beat 12..16
 // blocks and 256 workgroups by 15 - 20%.
 constexpr int kSplitWorkgroups = 512;
+// A split launch's workspace starts with a region of arrival counters of one fixed size,
+// whatever the shape, and its fp32 partial sums follow it.  Launches of different shapes that
+// share a workspace then find their counters at the same place: a counter region that grew
+// with the tile count would let one launch read another's left-over partial sums as counters.
+// Split plans have at most kSplitWorkgroups / 2 tiles (two splits or more each); forced plans
+// with more tiles than counters are refused.
+constexpr int kMaxCounterTiles = 1024;
+constexpr size_t kCounterBytes = size_t(kMaxCounterTiles) * 4u;
 
 // LDS layout of a workgroup whose K range has `tw` steps: activation row r at r * x_row,
 // x_row = 512 * tw + 16 (the pad puts the same 16-byte chunk of the 16 rows into 16
@@ -428,8 +436,10 @@ ResidentPlan plan_split(const GemmProblem* probs, int count, int g) {
     if (forced_split(fcb, fs)) {
         fs = fs < T ? fs : T;
         const int len = (T + fs - 1) / fs;
-        if (fs < 2 || len > kMaxLen || lds_bytes(len, g, fcb) > uint32_t(kMaxLds)) return ResidentPlan{};
-        return ResidentPlan{fcb, 1, len, fs, int(tiles_of(probs, count, fcb))};
+        const int64_t tiles = tiles_of(probs, count, fcb);
+        if (fs < 2 || len > kMaxLen || lds_bytes(len, g, fcb) > uint32_t(kMaxLds) || tiles > kMaxCounterTiles)
+            return ResidentPlan{};
+        return ResidentPlan{fcb, 1, len, fs, int(tiles)};
     }
     ResidentPlan best{};
     int64_t best_score = -1;
@@ -439,7 +449,7 @@ ResidentPlan plan_split(const GemmProblem* probs, int count, int g) {
         int s = int(kSplitWorkgroups / tiles);
         s = s < 1 ? 1 : (s > T ? T : s);
         const int len = (T + s - 1) / s;
-        if (s < 2 || len > kMaxLen || lds_bytes(len, g, cb) > uint32_t(kMaxLds)) continue;
+        if (s < 2 || len > kMaxLen || lds_bytes(len, g, cb) > uint32_t(kMaxLds) || tiles > kMaxCounterTiles) continue;
         // prefer workgroups up to the target, then whole column blocks in every tile, then
         // even ranges, then (first found) fewer waves per workgroup
         const int64_t wgs = tiles * s;
@@ -489,8 +499,7 @@ bool resident_preferred(const GemmProblem* probs, int count, int g, bool may_spl
 
 size_t resident_workspace_bytes(const ResidentPlan& pl) {
     if (pl.len == 0 || pl.splits <= 1) return 0;
-    const size_t counters = (size_t(pl.tiles) * 4 + 255) / 256 * 256;
-    return counters + size_t(pl.tiles) * size_t(pl.splits) * size_t(pl.cb) * 1024u;
+    return kCounterBytes + size_t(pl.tiles) * size_t(pl.splits) * size_t(pl.cb) * 1024u;
 }
 
 hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g, const ResidentPlan& pl,
@@ -511,10 +520,9 @@ hipError_t launch_gemm_resident_group(const GemmProblem* probs, int count, int g
     a.splits = pl.splits;
     a.tiles = total;
     if (pl.splits > 1) {
-        if (workspace == nullptr) return hipErrorInvalidValue;
-        const size_t counters = (size_t(total) * 4 + 255) / 256 * 256;
+        if (workspace == nullptr || total > kMaxCounterTiles) return hipErrorInvalidValue;
         a.counters = static_cast<uint32_t*>(workspace);
-        a.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + counters);
+        a.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kCounterBytes);
     }
     const int T = probs[0].K / kStepCodes;
     uint32_t lds = lds_bytes((T + pl.splits - 1) / pl.splits, g, pl.cb);

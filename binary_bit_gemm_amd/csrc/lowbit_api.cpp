@@ -5,6 +5,7 @@
 // allocates no device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -42,9 +43,9 @@ int check_pack_args(const void* codes, const void* W, int64_t N, int64_t K, int 
     return LOWBIT_OK;
 }
 
-// Cached gfx950 check per device ordinal: -1 unknown, 0 no, 1 yes.
-int g_dev_ok[64];
-bool g_dev_init = false;
+// Cached gfx950 check per device ordinal: 0 not yet probed, 1 no, 2 yes.  Threads that make
+// their first call at the same time may both probe; they store the same value.
+std::atomic<int> g_dev_ok[64];
 
 int device_check() {
     int dev = 0;
@@ -187,20 +188,18 @@ const char* lowbit_status_string(int status) {
 int lowbit_last_hip_error(void) { return g_last_hip_error; }
 
 int lowbit_device_supported(int device) {
-    if (!g_dev_init) {
-        for (int& v : g_dev_ok) v = -1;
-        g_dev_init = true;
-    }
     if (device < 0 || device >= 64) return 0;
-    if (g_dev_ok[device] >= 0) return g_dev_ok[device];
+    const int known = g_dev_ok[device].load(std::memory_order_relaxed);
+    if (known != 0) return known - 1;
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess) {
         g_last_hip_error = int(e);
         return -LOWBIT_E_HIP;
     }
-    g_dev_ok[device] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
-    return g_dev_ok[device];
+    const int ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    g_dev_ok[device].store(ok + 1, std::memory_order_relaxed);
+    return ok;
 }
 
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,

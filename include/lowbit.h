@@ -129,6 +129,9 @@ int lowbit_import_ternary(const void* src, int layout, int zero, uint32_t* W, in
  *   W    device, N*K/32 uint32, written.
  *   Requires N % 16 == 0, K % 32 == 0, K <= 2^22, 16-byte aligned src and W.  Scales are the
  *   caller's (the card's per-group fp16 scale_g is the library's scale).
+ *   The byte layout is a reading, not a published format: the card names the GemLite 1-bit
+ *   pack without describing its bits, so this importer's parity against real GemLite files is
+ *   unpinned (none is available); only its self-consistency with lowbit_pack is tested.
  */
 int lowbit_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t N, int64_t K, void* stream);
 
@@ -181,9 +184,11 @@ size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits);
 /*
  * lowbit_gemm_ex -- lowbit_gemm with a caller-provided workspace.
  *   workspace        device memory of at least lowbit_workspace_size(...) bytes, 16-byte
- *                    aligned, ZERO-FILLED before its first use.  Every call leaves the
- *                    workspace's counters at zero again, so it can be reused as is.  Calls
- *                    that share a workspace must not run concurrently.
+ *                    aligned, ZERO-FILLED before its first use.  Its first 4096 bytes hold
+ *                    arrival counters at the same place for every shape; every call leaves
+ *                    them at zero again, so one workspace serves calls of any shapes in
+ *                    turn as is (the rest holds partial sums, which need no clearing).
+ *                    Calls that share a workspace must not run concurrently.
  *   workspace_bytes  its size.  With a NULL or too small workspace (or for shapes that need
  *                    none) the call is exactly lowbit_gemm.
  */
@@ -210,9 +215,10 @@ int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* work
  *   X  device bf16 [M, K];  W  device packed words [2N, K*bits/32];
  *   S  device fp16 [2N, K/g];  Y  device bf16 [M, N], fully overwritten.
  * Both factors are the fp32 sums of lowbit_gemm's arithmetic; the product is rounded to
- * bf16 once.  Supports g = 64 or 128 (both bit widths); g = 32 returns LOWBIT_E_UNSUPPORTED.
- * Runs on the large-M tile kernel for every M (small M computes correctly but at that
- * kernel's speed).  Argument checks and errors as lowbit_gemm, with 2N weight rows.
+ * bf16 once.  Supports g = 64 or 128 (all bit widths); g = 32 returns LOWBIT_E_UNSUPPORTED.
+ * Ternary problems with M <= 16 whose whole K fits one workgroup run on the skinny resident
+ * kernel; every other shape runs on the 16x16-block tile kernel.  Argument checks and errors
+ * as lowbit_gemm, with 2N weight rows.
  */
 int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
                        int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);

@@ -14,6 +14,8 @@ from tests.gpu_helpers import dev_codes, dev_scales, dev_x, host_bits, run_gemm,
 pytestmark = pytest.mark.gpu
 
 REL_ALARM = 2.5e-3
+# the arrival counters of a split launch: the workspace's first 4 KiB, whatever the shape
+COUNTER_BYTES = 4096
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,7 +67,7 @@ def test_split_through_workspace(N, K, g):
     y2 = host_bits(lb.gemm(x, w, s, g, 2, workspace=ws))
     torch().cuda.synchronize()
     assert np.array_equal(y1, y2)
-    assert not ws[:256].any().item(), "arrival counters not reset"
+    assert not ws[:COUNTER_BYTES].any().item(), "arrival counters not reset"
 
 
 @pytest.mark.parametrize("M", [1, 3, 8, 15])
@@ -87,7 +89,7 @@ def test_one_workspace_for_every_shape():
         x, w, s = _dev(inp)
         y = host_bits(lb.gemm(x, w, s, 64, 2, workspace=ws))
         _check(y, inp, 64, f"shared workspace {N}x{K}")
-    assert not ws[:256].any().item()
+    assert not ws[:COUNTER_BYTES].any().item()
 
 
 def test_batched_pairs_through_workspace():
@@ -110,7 +112,7 @@ def test_batched_pairs_through_workspace():
         for i, inp in enumerate(inps):
             assert np.array_equal(first[i], host_bits(probs[i][3])), f"{N}x{K} problem {i} not deterministic"
             _check(first[i], inp, 64, f"batched {N}x{K} problem {i} ws={n}")
-        assert not ws[:256].any().item()
+        assert not ws[:COUNTER_BYTES].any().item()
 
 
 def test_ex_falls_back_without_enough_workspace():
@@ -166,3 +168,31 @@ def test_default_choice_large_n_whole_k():
     assert np.array_equal(y1, y2)
     cols = np.random.default_rng(0).choice(27648, 2048, replace=False)
     _check(y1[:, cols], W.Inputs(inp.x, inp.codes[cols], inp.scales[cols]), 64, "N=27648 sampled columns")
+
+
+def test_workspace_shared_by_launches_of_different_tile_counts():
+    """One workspace serves a split launch with few column groups (16x3072x12288: 32 tiles),
+    then launches with many (16x18432x6144: 128 tiles), as single calls and as a batched call
+    that mixes both K.  The first launch leaves its fp32 partial sums in the workspace; every
+    later launch must still find its arrival counters at zero and every result must meet the
+    oracle."""
+    t = torch()
+    small, large = (3072, 12288), (18432, 6144)
+    need = max(lb.workspace_size(16, N, K, 64, 2) for N, K in (small, large))
+    items = []
+    for i, (N, K) in enumerate((small, large, small, large)):
+        inp = _inputs(16, N, K, 64, seed=20 + i, cid=84)
+        x, w, s = _dev(inp)
+        items.append((inp, (x, w, s, t.empty((16, N), dtype=t.bfloat16, device="cuda"), 64, 2)))
+    need = max(need, lb.batched_workspace_size([a for _, a in items]))
+    ws = _workspace(need)
+    for rep in range(2):
+        for inp, (x, w, s, y, g, bits) in items[:2]:
+            yb = host_bits(lb.gemm(x, w, s, g, bits, workspace=ws))
+            _check(yb, inp, g, f"shared workspace {tuple(x.shape)}x{w.shape[0]} pass {rep}")
+            assert not ws[:COUNTER_BYTES].any().item(), "arrival counters not reset"
+    lb.gemm_batched([a for _, a in items], workspace=ws)
+    t.cuda.synchronize()
+    for inp, (x, w, s, y, g, bits) in items:
+        _check(host_bits(y), inp, g, f"batched, shared workspace {tuple(x.shape)}x{w.shape[0]}")
+    assert not ws[:COUNTER_BYTES].any().item(), "arrival counters not reset"
