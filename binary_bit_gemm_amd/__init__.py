@@ -184,6 +184,33 @@ def gemm(x, words, scales, g: int, bits: int, out=None, workspace=None):
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 4096 + 512 * 16 * 1024  # LOWBIT_NOALLOC_SCRATCH_BYTES of include/lowbit.h
+
+
+def gemm_noalloc(x, words, scales, g: int, bits: int, out):
+    """lowbit_gemm_noalloc: lowbit_gemm_ex on the library's static per-GPU scratch, for callers
+    that cannot allocate (`out` is required: this call allocates nothing).  Calls on one GPU
+    share the scratch and must not overlap."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    _require(words, torch.int32, "words")
+    _require(scales, torch.float16, "scales")
+    _require(out, torch.bfloat16, "out")
+    M, K = x.shape
+    N = words.shape[0]
+    if words.shape[1] != words_per_row(K, bits):
+        raise ValueError(f"words must be [N, K*bits/32] = [{N}, {words_per_row(K, bits)}], got {tuple(words.shape)}")
+    if K % g or tuple(scales.shape) != (N, K // g):
+        raise ValueError(f"scales must be [N, K/g] = [{N}, {K // g if g else 0}], got {tuple(scales.shape)}")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    st = lib().lowbit_gemm_noalloc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                                   ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                   M, N, K, g, bits, ctypes.c_void_p(_stream_ptr(x.device)))
+    _check(st, "lowbit_gemm_noalloc")
+    return out
+
+
 class Problem(ctypes.Structure):
     _fields_ = [("X", ctypes.c_void_p), ("W", ctypes.c_void_p), ("S", ctypes.c_void_p), ("Y", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),

@@ -167,6 +167,40 @@ int batched(const lowbit_problem* problems, int count, void* workspace, size_t w
     });
 }
 
+// ---- static scratch of lowbit_gemm_noalloc ----
+// The split-K workspace of the resident kernel, for callers that cannot allocate: one array
+// per device, held from the library's load until the process ends.  Its size is the largest
+// workspace an automatic split plan asks for (the 4 KiB counter region plus at most
+// 512 workgroups x 16 column blocks x 1 KiB of fp32 partial sums).  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address hipGetSymbolAddress returns
+// for the current device (kept per device below) is passed to kernels.
+static_assert(LOWBIT_NOALLOC_SCRATCH_BYTES == 4096 + 512 * 16 * 1024, "scratch size");
+static __device__ __align__(256) unsigned char scratch[LOWBIT_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_dev[64];
+constexpr int kCounterWords = 1024;  // the workspace's counter region (first 4 KiB)
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+    const int i = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
+    if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch address, looked up once per device (the device must be current).
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return LOWBIT_E_UNSUPPORTED;
+    void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (ptr == nullptr) return LOWBIT_E_HIP;
+        g_scratch_dev[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return LOWBIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +215,7 @@ const char* lowbit_status_string(int status) {
         case LOWBIT_E_ALIGN: return "tensor pointer not 16-byte aligned";
         case LOWBIT_E_HIP: return "HIP runtime error (see lowbit_last_hip_error)";
         case LOWBIT_E_TOO_MANY: return "too many problems in one batched call";
+        case LOWBIT_E_SCRATCH: return "the shape needs more workspace than the static scratch of lowbit_gemm_noalloc holds";
         default: return "unknown status";
     }
 }
@@ -358,6 +393,31 @@ int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y, int
                           static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
     const hipError_t e = lowbit::launch_gemm_grouped(&p, 1, g, bits, workspace, workspace_bytes,
                                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
+int lowbit_gemm_noalloc(const void* X, const uint32_t* W, const void* S, void* Y, int64_t M, int64_t N, int64_t K,
+                        int g, int bits, void* stream) {
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    const size_t need = lowbit_workspace_size(M, N, K, g, bits);
+    if (need > LOWBIT_NOALLOC_SCRATCH_BYTES) return LOWBIT_E_SCRATCH;
+    if (need == 0 || forced_variant() >= 0) return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != LOWBIT_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // the arrival counters must start at zero: every call leaves them so, and a fill kernel
+    // (not a memset, which a captured graph must not hold) clears them again first
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(kCounterWords / 256), dim3(256), 0, s, static_cast<uint32_t*>(ws),
+                       kCounterWords);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+    lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                          static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
+    e = lowbit::launch_gemm_grouped(&p, 1, g, bits, ws, LOWBIT_NOALLOC_SCRATCH_BYTES, s);
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 

@@ -67,7 +67,8 @@ enum {
     LOWBIT_E_UNSUPPORTED = 2, /* bits / g or a size outside the supported set, or device not gfx950 */
     LOWBIT_E_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned                   */
     LOWBIT_E_HIP = 4,         /* a HIP runtime call failed; see lowbit_last_hip_error()    */
-    LOWBIT_E_TOO_MANY = 5     /* batched call: more problems than one call accepts         */
+    LOWBIT_E_TOO_MANY = 5,    /* batched call: more problems than one call accepts         */
+    LOWBIT_E_SCRATCH = 6      /* lowbit_gemm_noalloc: the shape needs more than its scratch */
 };
 
 /*
@@ -195,6 +196,24 @@ size_t lowbit_workspace_size(int64_t M, int64_t N, int64_t K, int g, int bits);
 int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y,
                    int64_t M, int64_t N, int64_t K, int g, int bits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lowbit_gemm_noalloc -- lowbit_gemm_ex without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * lowbit_gemm_ex given a large enough workspace.
+ *   The workspace is a static device array of LOWBIT_NOALLOC_SCRATCH_BYTES per GPU, held from
+ *   the library's load until the process ends; it covers every automatic split plan.  A shape
+ *   whose lowbit_workspace_size exceeds it returns LOWBIT_E_SCRATCH and launches nothing
+ *   (only a forced split plan can).  Shapes that need no workspace run as lowbit_gemm.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ *   streams, other host threads) race and must be serialised by the caller.  Each call first
+ *   clears the array's counter region with a fill kernel on `stream` (no memset).
+ *   The call allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ */
+#define LOWBIT_NOALLOC_SCRATCH_BYTES (4096u + 512u * 16u * 1024u)
+int lowbit_gemm_noalloc(const void* X, const uint32_t* W, const void* S, void* Y,
+                        int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
 
 /*
  * lowbit_batched_workspace_size / lowbit_gemm_batched_ex -- lowbit_gemm_batched with a

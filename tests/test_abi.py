@@ -244,3 +244,23 @@ def test_gemm_ex_validates_before_the_device():
     assert L.lowbit_gemm_ex(None, A, A, A, 16, 3072, 3072, 64, 2, A, 1 << 20, None) == INVALID
     assert L.lowbit_gemm_ex(A, A, A, A, 16, 3072, 3072, 64, 3, A, 1 << 20, None) == UNSUPPORTED
     assert L.lowbit_gemm_ex(A, A, A, A, 0, 3072, 3072, 64, 2, None, 0, None) == OK
+
+
+SCRATCH = 6
+
+
+def test_noalloc_validates_before_the_device(monkeypatch):
+    L = lb.lib()
+    A = 256
+    assert lb.status_string(SCRATCH) and lb.status_string(SCRATCH) != "unknown status"
+    assert L.lowbit_gemm_noalloc(None, A, A, A, 16, 3072, 3072, 64, 2, None) == INVALID
+    assert L.lowbit_gemm_noalloc(A, A, A, A + 8, 16, 3072, 3072, 64, 2, None) == ALIGN
+    assert L.lowbit_gemm_noalloc(A, A, A, A, 16, 3072, 3072, 64, 3, None) == UNSUPPORTED
+    assert L.lowbit_gemm_noalloc(A, A, A, A, 0, 3072, 3072, 64, 2, None) == OK
+    # every automatic split plan fits the static scratch ...
+    for (M, N, K) in ((16, 3072, 12288), (16, 18432, 9216), (1, 4096, 65536), (8, 18432, 12288)):
+        assert 0 < lb.workspace_size(M, N, K, 64, 2) <= lb.NOALLOC_SCRATCH_BYTES, (M, N, K)
+    # ... a forced plan that needs more is refused before anything touches a device
+    monkeypatch.setenv("LOWBIT_RESIDENT_PLAN", "1,16")
+    assert lb.workspace_size(16, 16384, 16384, 64, 2) > lb.NOALLOC_SCRATCH_BYTES
+    assert L.lowbit_gemm_noalloc(A, A, A, A, 16, 16384, 16384, 64, 2, None) == SCRATCH
