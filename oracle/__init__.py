@@ -19,6 +19,9 @@ define (see each docstring for the passage):
 * other runtimes' ternary packs: GemLite's int2 weights, uint8 packed over K with a
   transpose, (in_features / 4, out_features) (Bonsai-Image-Demo pull request 20, "CPU
   bring-up"), and MLX's packed uint32 rows (the "Checkpoint layout" section above);
+* the 4-bit text encoder: loaded quantised at bits = 4, group_size = 64 (the mlx guide,
+  section "组件架构"), dequantised through HQQ on the CPU (pull request 20); its groups are
+  read as affine, w = s * q + b (reading R10 of `oracle.lowbit_ref`);
 * the reference computation is dequantise-to-dense followed by an ordinary matmul
   (Bonsai-Image-Demo pull request 20, "CPU image bring-up report": the validated CPU
   path runs the unpacked dense transformer).
@@ -36,5 +39,6 @@ from .lowbit_ref import (  # noqa: F401
     silu_f64, swiglu_ref_f64, residual_ref_f64,
     gemlite_u8t_decode, gemlite_u8t_encode, mlx_u32_decode, mlx_u32_encode,
     gemlite_binary_decode, gemlite_binary_encode,
+    pack_u4, unpack_u4, dequant_affine_f64, gemm_affine_ref_f64, gemm_affine_fsum_element,
     check_tolerance, REL_FROB_TOL, ELEM_TOL,
 )

@@ -40,6 +40,13 @@ R9  4-bit codes (the 4-bit text encoder of the binary model card's "Model Overvi
     integers c in [-8, 7] as two's complement nibbles, 8 per uint32 along K, least significant
     first (code k at bits 4*(k % 8) of word k // 8), with the symmetric form w = s * c of R4.
     The card names only "4-bit HQQ"; its zero points are not on the pages.
+R10 Affine 4-bit groups of the text encoder: the mlx guide (section "组件架构") loads the
+    4-bit Qwen3 text encoder quantised with bits = 4, group_size = 64, and the CPU bring-up
+    (Bonsai-Image-Demo pull request 20) dequantises the HQQ text encoder.  Both runtimes' 4-bit
+    groups are affine; the plainest common form is w = s * q + b with unsigned levels
+    q in [0, 15] and one fp16 scale s and one fp16 bias b per group of g consecutive weights
+    along K (an HQQ zero point z is b = -z * s).  Levels are packed 8 per uint32, least
+    significant nibble first (level k at bits 4*(k % 8) of word k // 8), like R9.
 """
 from __future__ import annotations
 
@@ -311,6 +318,75 @@ def residual_ref_f64(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, 
     if r.shape != y.shape or gt.shape != (y.shape[1],):
         raise ValueError("residual must be [M, N] and gate [N]")
     return r + gt[None, :] * y
+
+
+# ----------------------------------------------------------------------------------------
+# Affine 4-bit groups (reading R10)
+# ----------------------------------------------------------------------------------------
+
+def pack_u4(levels: np.ndarray) -> Tuple[np.ndarray, int]:
+    """Unsigned 4-bit levels [N, K] (0 .. 15) -> (uint32 words [N, K/8], number of invalid
+    levels).  Level k of a row sits at bits 4*(k % 8) of word k // 8; levels outside 0 .. 15
+    pack as 0 and are counted."""
+    q = np.asarray(levels, dtype=np.int64)
+    if q.ndim != 2 or q.shape[1] % 8:
+        raise ValueError("levels must be [N, K] with K a multiple of 8")
+    N, K = q.shape
+    ok = (q >= 0) & (q <= 15)
+    field = np.where(ok, q, 0).astype(np.uint32).reshape(N, K // 8, 8)
+    words = np.zeros((N, K // 8), dtype=np.uint32)
+    for i in range(8):
+        words |= field[:, :, i] << np.uint32(4 * i)
+    return words, int(np.count_nonzero(~ok))
+
+
+def unpack_u4(words: np.ndarray, K: int) -> np.ndarray:
+    """uint32 words [N, K/8] -> unsigned levels [N, K] (uint8, 0 .. 15)."""
+    w = np.asarray(words, dtype=np.uint32)
+    N = w.shape[0]
+    if w.shape[1] * 8 != K:
+        raise ValueError("words do not hold K levels per row")
+    out = np.zeros((N, w.shape[1], 8), dtype=np.uint8)
+    for i in range(8):
+        out[:, :, i] = ((w >> np.uint32(4 * i)) & np.uint32(15)).astype(np.uint8)
+    return out.reshape(N, K)
+
+
+def dequant_affine_f64(levels: np.ndarray, scales: np.ndarray, biases: np.ndarray, g: int) -> np.ndarray:
+    """W[n, k] = q[n, k] * S[n, k // g] + B[n, k // g] in fp64.  Exact: q * s has at most
+    4 + 11 significant bits and adding the fp16 bias needs far fewer than fp64's 53."""
+    q = np.asarray(levels).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    b = np.asarray(biases, dtype=np.float16).astype(np.float64)
+    N, K = q.shape
+    if K % g or s.shape != (N, K // g) or b.shape != (N, K // g):
+        raise ValueError("scales and biases must be [N, K // g]")
+    return q * np.repeat(s, g, axis=1) + np.repeat(b, g, axis=1)
+
+
+def gemm_affine_ref_f64(x_bits: np.ndarray, levels: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                        g: int) -> np.ndarray:
+    """Y = X @ dequant_affine(W).T in fp64: dequantise to dense, then an ordinary matmul."""
+    xd = bf16_bits_to_f64(x_bits)
+    wd = dequant_affine_f64(levels, scales, biases, g)
+    if xd.shape[1] != wd.shape[1]:
+        raise ValueError("X and W disagree on K")
+    return xd @ wd.T
+
+
+def gemm_affine_fsum_element(x_bits: np.ndarray, levels: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                             g: int, m: int, n: int) -> float:
+    """One affine output element as the correctly rounded sum (math.fsum) of its exact terms
+    x * q * s and x * b."""
+    x = bf16_bits_to_f64(np.asarray(x_bits)[m])
+    q = np.asarray(levels)[n]
+    s = np.asarray(scales, dtype=np.float16)[n].astype(np.float64)
+    b = np.asarray(biases, dtype=np.float16)[n].astype(np.float64)
+    terms = []
+    for k in range(q.shape[0]):
+        terms.append(float(x[k]) * int(q[k]) * float(s[k // g]))
+        terms.append(float(x[k]) * float(b[k // g]))
+    return math.fsum(terms)
 
 
 # ----------------------------------------------------------------------------------------

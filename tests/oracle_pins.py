@@ -41,7 +41,11 @@ def real_oracle():
                            gemlite_u8t_decode=oracle.gemlite_u8t_decode, gemlite_u8t_encode=oracle.gemlite_u8t_encode,
                            mlx_u32_decode=oracle.mlx_u32_decode, mlx_u32_encode=oracle.mlx_u32_encode,
                            gemlite_binary_decode=oracle.gemlite_binary_decode,
-                           gemlite_binary_encode=oracle.gemlite_binary_encode)
+                           gemlite_binary_encode=oracle.gemlite_binary_encode,
+                           pack_u4=oracle.pack_u4, unpack_u4=oracle.unpack_u4,
+                           dequant_affine_f64=oracle.dequant_affine_f64,
+                           gemm_affine_ref_f64=oracle.gemm_affine_ref_f64,
+                           gemm_affine_fsum_element=oracle.gemm_affine_fsum_element)
 
 
 # ----------------------------------------------------------------------------------------
@@ -496,3 +500,116 @@ def pin_int4_fsum(o):
 
 
 INT4_PINS = [pin_int4_hex_words, pin_int4_one_hot, pin_int4_fsum]
+
+
+# ----------------------------------------------------------------------------------------
+# Affine 4-bit groups: w = s * q + b, unsigned levels q in [0, 15] (reading R10)
+
+GOLDEN_U4 = os.path.join(os.path.dirname(__file__), "golden", "pack_u4_words.txt")
+
+
+def load_golden_u4():
+    rows = []
+    with open(GOLDEN_U4) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, levels, word = [s.strip() for s in line.split("|")]
+            rows.append((name, np.array([int(v) for v in levels.split(",")], dtype=np.int64), int(word, 16)))
+    return rows
+
+
+def _affine_case(seed, M, N, K, g):
+    rng = rng_for(seed, 97, 0)
+    x = gen_x(rng, M, K)
+    q = rng.integers(0, 16, size=(N, K))
+    s = gen_scales(rng, N, K, g)
+    b = (-rng.uniform(0.0, 0.4, size=(N, K // g))).astype(np.float16)
+    return x, q, s, b
+
+
+def pin_u4_words(o, seed=61):
+    """Unsigned level words equal the hand-worked golden words and integers parsed from hex
+    strings written most-significant nibble first (the digit of q looked up in
+    "0123456789ABCDEF", not computed by the packer's rule); unpacking returns the levels;
+    levels outside 0 .. 15 are packed as 0 and counted."""
+    for name, levels, word in load_golden_u4():
+        w, bad = o.pack_u4(levels[None, :])
+        assert bad == 0 and w.shape == (1, 1) and int(w[0, 0]) == word, f"{name}: {int(w[0, 0]):#010x}"
+        assert np.array_equal(o.unpack_u4(np.array([[word]], dtype=np.uint32), 8)[0], levels), name
+    digits = "0123456789ABCDEF"
+    q = np.random.default_rng(seed).integers(0, 16, size=(5, 64))
+    w, bad = o.pack_u4(q)
+    assert bad == 0 and w.shape == (5, 8)
+    for n in range(5):
+        for j in range(8):
+            assert int(w[n, j]) == int("".join(digits[int(v)] for v in reversed(q[n, 8 * j:8 * j + 8])), 16), (n, j)
+    assert np.array_equal(o.unpack_u4(w, 64), q)
+    w, bad = o.pack_u4(np.array([[16, -1, 200, 1, 0, 0, 15, 0]]))
+    assert bad == 3 and int(w[0, 0]) == 0x0F001000
+
+
+def pin_affine_group_sums(o):
+    """X = 1 on the run of group j of row j (0 elsewhere): Y[j, n] = s[n, j] * (sum of the run's
+    levels) + g * b[n, j], a closed form evaluated with integer level sums.  A bias taken from
+    the wrong group, dropped, or multiplied by the level fails it."""
+    g, G = 64, 4
+    K, N = g * G, 16
+    _, q, s, b = _affine_case(5, 1, N, K, g)
+    x = np.zeros((G, K), dtype=np.uint16)
+    for j in range(G):
+        x[j, j * g:(j + 1) * g] = 0x3F80  # bf16 1.0
+    w, _ = o.pack_u4(q)
+    y = o.gemm_affine_ref_f64(x, o.unpack_u4(w, K), s, b, g)
+    for j in range(G):
+        for n in range(N):
+            want = float(s[n, j]) * int(q[n, j * g:(j + 1) * g].sum()) + g * float(b[n, j])
+            assert abs(y[j, n] - want) <= 1e-12 * (abs(want) + 1), (j, n, y[j, n], want)
+
+
+def pin_affine_is_symmetric_shifted(o, seed=63):
+    """With b = -8 s (exact in fp16) and q = c + 8 for two's complement codes c in [-8, 7], the
+    affine weight equals the symmetric 4-bit weight s * c: the affine GEMM must equal the pinned
+    symmetric oracle exactly, through packing and unpacking of the levels."""
+    M, N, K, g = 8, 32, 256, 64
+    x, _, s, _ = _affine_case(seed, M, N, K, g)
+    c = gen_codes(rng_for(seed, 97, 1), N, K, 4)
+    b = (np.float16(-8.0) * s).astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), -8.0 * s.astype(np.float64))
+    w, bad = o.pack_u4(c.astype(np.int64) + 8)
+    assert bad == 0
+    y = o.gemm_affine_ref_f64(x, o.unpack_u4(w, K), s, b, g)
+    assert np.array_equal(y, o.gemm_ref_f64(x, c, s, g))
+
+
+def pin_affine_fsum(o, seed=65):
+    """The affine GEMM against math.fsum of its exact terms, within the fp64 summation bound."""
+    M, N, K, g = 6, 24, 256, 64
+    x, q, s, b = _affine_case(seed, M, N, K, g)
+    y = o.gemm_affine_ref_f64(x, q, s, b, g)
+    xf = o.bf16_bits_to_f64(x)
+    wabs = np.abs(q * np.repeat(s.astype(np.float64), g, 1)) + np.abs(np.repeat(b.astype(np.float64), g, 1))
+    bound = 4 * K * 2.0 ** -53 * (np.abs(xf) @ wabs.T)
+    for m in range(M):
+        for n in range(N):
+            e = o.gemm_affine_fsum_element(x, q, s, b, g, m, n)
+            assert abs(y[m, n] - e) <= bound[m, n] + 1e-300, (m, n)
+
+
+def pin_affine_bias_only(o, seed=67):
+    """Zero scales leave only the bias term: Y[m, n] = sum_g b[n, g] * (sum of X[m, k] over group
+    g), evaluated with math.fsum over the activations of each group (no weight is formed)."""
+    M, N, K, g = 4, 16, 192, 64
+    x, q, s, b = _affine_case(seed, M, N, K, g)
+    s = np.zeros_like(s)
+    y = o.gemm_affine_ref_f64(x, q, s, b, g)
+    xf = o.bf16_bits_to_f64(x)
+    for m in range(M):
+        rs = [math.fsum(float(v) for v in xf[m, j * g:(j + 1) * g]) for j in range(K // g)]
+        for n in range(N):
+            want = math.fsum(float(b[n, j]) * rs[j] for j in range(K // g))
+            assert abs(y[m, n] - want) <= 1e-12 * (abs(want) + 1), (m, n)
+
+
+AFFINE_PINS = [pin_u4_words, pin_affine_group_sums, pin_affine_is_symmetric_shifted, pin_affine_fsum,
+               pin_affine_bias_only]

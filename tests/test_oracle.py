@@ -10,7 +10,7 @@ from oracle import lowbit_ref as ref
 from tests import oracle_pins as P
 
 
-@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS + P.IMPORT_PINS + P.INT4_PINS,
+@pytest.mark.parametrize("pin", P.ALL_PINS + P.SWIGLU_PINS + P.RESIDUAL_PINS + P.IMPORT_PINS + P.INT4_PINS + P.AFFINE_PINS,
                          ids=lambda f: f.__name__)
 def test_pin_holds(pin):
     pin(P.real_oracle())
@@ -398,3 +398,54 @@ def test_int4_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError):
             failures.append(pin.__name__)
     assert failures, f"planted mistake {name} passed every 4-bit pin"
+
+
+# planted affine 4-bit mistakes: signed nibbles, most-significant nibble first (pack and unpack
+# alike), the bias dropped, the bias multiplied by the level, and the first group's bias used for
+# every group
+
+
+def _u4_signed_unpack(words, K):
+    q = oracle.unpack_u4(words, K).astype(np.int64)
+    return np.where(q >= 8, q - 16, q)
+
+
+def _u4_msb_pack(levels):
+    q = np.asarray(levels)
+    return oracle.pack_u4(q.reshape(q.shape[0], -1, 8)[:, :, ::-1].reshape(q.shape))
+
+
+def _u4_msb_unpack(words, K):
+    q = oracle.unpack_u4(words, K)
+    return q.reshape(q.shape[0], -1, 8)[:, :, ::-1].reshape(q.shape)
+
+
+def _affine_with_weight(fn):
+    def gemm(x_bits, levels, scales, biases, g):
+        q = np.asarray(levels).astype(np.float64)
+        s = np.repeat(np.asarray(scales, dtype=np.float16).astype(np.float64), g, axis=1)
+        b = np.repeat(np.asarray(biases, dtype=np.float16).astype(np.float64), g, axis=1)
+        return oracle.bf16_bits_to_f64(x_bits) @ fn(q, s, b, np.asarray(biases, dtype=np.float16), g).T
+    return gemm
+
+
+AFFINE_PLANTED = {
+    "u4_signed_nibbles": dict(unpack_u4=_u4_signed_unpack),
+    "u4_msb_first": dict(pack_u4=_u4_msb_pack, unpack_u4=_u4_msb_unpack),
+    "affine_bias_dropped": dict(gemm_affine_ref_f64=_affine_with_weight(lambda q, s, b, b0, g: q * s)),
+    "affine_bias_times_level": dict(gemm_affine_ref_f64=_affine_with_weight(lambda q, s, b, b0, g: q * (s + b))),
+    "affine_first_group_bias": dict(gemm_affine_ref_f64=_affine_with_weight(
+        lambda q, s, b, b0, g: q * s + b0[:, :1].astype(np.float64))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AFFINE_PLANTED))
+def test_affine_planted_mistake_is_caught(name):
+    broken = SimpleNamespace(**{**vars(P.real_oracle()), **AFFINE_PLANTED[name]})
+    failures = []
+    for pin in P.AFFINE_PINS:
+        try:
+            pin(broken)
+        except (AssertionError, ValueError, IndexError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passed every affine pin"

@@ -68,6 +68,20 @@ def gen_codes(rng: np.random.Generator, N: int, K: int, bits: int) -> np.ndarray
     raise ValueError(f"bits must be 1, 2 or 4, got {bits}")
 
 
+def gen_levels(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """Unsigned 4-bit levels of affine groups, shape [N, K], uniform on 0 .. 15 (int8)."""
+    return rng.integers(0, 16, size=(N, K), dtype=np.int8)
+
+
+def gen_biases(rng: np.random.Generator, N: int, K: int, g: int) -> np.ndarray:
+    """fp16 group biases of affine groups, shape [N, K // g], uniform on [-0.45, -0.03]: the
+    range of -z * s for zero points z in [6, 9] and the scales of gen_scales, drawn
+    independently of the scales."""
+    if K % g:
+        raise ValueError("K must be a multiple of g")
+    return rng.uniform(-0.45, -0.03, size=(N, K // g)).astype(np.float16)
+
+
 def gen_scales(rng: np.random.Generator, N: int, K: int, g: int) -> np.ndarray:
     """fp16 group scales, shape [N, K // g], uniform on [0.005, 0.05]."""
     if K % g:
@@ -86,6 +100,7 @@ class Problem:
     g: int = 64
     config_id: int = 0
     tensor_id: int = 0
+    affine: bool = False   # 4-bit affine groups: levels 0 .. 15 with a scale and a bias per group
 
     @property
     def flops(self) -> int:
@@ -93,15 +108,17 @@ class Problem:
 
     def bytes_moved(self) -> int:
         """Algorithmic HBM bytes: X + packed W + fp16 scales + Y."""
+        groups = 2 if self.affine else 1  # fp16 scales (and biases)
         return (2 * self.M * self.K + self.N * self.K * self.bits // 8
-                + 2 * self.N * (self.K // self.g) + 2 * self.M * self.N)
+                + 2 * groups * self.N * (self.K // self.g) + 2 * self.M * self.N)
 
 
 @dataclasses.dataclass
 class Inputs:
     x: np.ndarray       # uint16 bf16 bits [M, K]
-    codes: np.ndarray   # int8 [N, K]
+    codes: np.ndarray   # int8 [N, K] (affine problems: the unsigned levels 0 .. 15)
     scales: np.ndarray  # float16 [N, K // g]
+    biases: np.ndarray | None = None  # float16 [N, K // g], affine problems only
 
 
 def make_inputs(p: Problem, seed: int = 0, x_tensor_id: int | None = None) -> Inputs:
@@ -111,6 +128,11 @@ def make_inputs(p: Problem, seed: int = 0, x_tensor_id: int | None = None) -> In
     base = p.tensor_id * 3
     xid = base if x_tensor_id is None else x_tensor_id
     x = gen_x(rng_for(seed, p.config_id, xid), p.M, p.K)
+    if p.affine:
+        levels = gen_levels(rng_for(seed, p.config_id, base + 1), p.N, p.K)
+        scales = gen_scales(rng_for(seed, p.config_id, base + 2), p.N, p.K, p.g)
+        biases = gen_biases(rng_for(seed, p.config_id, 100000 + p.tensor_id), p.N, p.K, p.g)
+        return Inputs(x, levels, scales, biases)
     codes = gen_codes(rng_for(seed, p.config_id, base + 1), p.N, p.K, p.bits)
     scales = gen_scales(rng_for(seed, p.config_id, base + 2), p.N, p.K, p.g)
     return Inputs(x, codes, scales)
