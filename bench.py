@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="res1024",
                     choices=["res1024", "res1024_binary", "res512", "res512_binary", "sweep", "skinny", "swiglu",
-                             "swiglu16", "residual", "te4"])
+                             "swiglu16", "residual", "te4", "te4_sym"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -127,11 +127,14 @@ def problems_for(workload):
     if workload == "residual":
         # the MLP-out linear at 1024^2 (M = 4608, 9216 -> 3072) with its gated residual update fused
         return [W.Problem("m4608_mlp_out_residual", 4608, 3072, 9216, W.TERNARY, 64, 3, 3)]
-    if workload == "te4":
+    if workload in ("te4", "te4_sym"):
         # the 4-bit text encoder's MLP at a 512-token prompt (hidden 2560, intermediate 9728): gate
-        # and up fused into one 2560 -> 19456 linear, then down 9728 -> 2560; two dependent launches
-        return [W.Problem("te_mlp_gate_up", 512, 19456, 2560, W.INT4, 64, 6, 0),
-                W.Problem("te_mlp_down", 512, 2560, 9728, W.INT4, 64, 6, 1)]
+        # and up fused into one 2560 -> 19456 linear, then down 9728 -> 2560; two dependent launches.
+        # te4: affine groups (levels 0..15, a scale and a bias per group of 64); te4_sym: the
+        # symmetric signed form
+        affine = workload == "te4"
+        return [W.Problem("te_mlp_gate_up", 512, 19456, 2560, W.INT4, 64, 6, 0, affine=affine),
+                W.Problem("te_mlp_down", 512, 2560, 9728, W.INT4, 64, 6, 1, affine=affine)]
     if workload == "swiglu16":
         # the same linear at M = 16 (the skinny denoise-step row count)
         return [W.Problem("m16_mlp_in_swiglu", 16, 18432, 3072, W.TERNARY, 64, 3, 2)]
@@ -156,11 +159,23 @@ def make_device_inputs(probs, seed):
     gen = torch.Generator(device="cuda")
     lut = torch.tensor([-1, 0, 0, 1], dtype=torch.int8, device="cuda")
     bufs = []
+    biases = {}  # affine problems: fp16 group biases
     for i, p in enumerate(probs):
         gen.manual_seed(seed * 1000003 + p.config_id * 1009 + p.tensor_id)
         x = torch.randn((p.M, p.K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        if p.affine:
+            levels = torch.randint(0, 16, (p.N, p.K), generator=gen, device="cuda", dtype=torch.uint8)
+            words, _ = lb.pack_u4(levels, count_invalid=False)
+            del levels
+            s = (torch.rand((p.N, p.K // p.g), generator=gen, device="cuda") * 0.045 + 0.005).to(torch.float16)
+            biases[i] = (torch.rand((p.N, p.K // p.g), generator=gen, device="cuda") * -0.42 - 0.03).to(torch.float16)
+            y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+            bufs.append((x, words, s, y, p.g, p.bits))
+            continue
         if p.bits == 2:
             codes = lut[torch.randint(0, 4, (p.N, p.K), generator=gen, device="cuda")]
+        elif p.bits == 4:
+            codes = torch.randint(-8, 8, (p.N, p.K), generator=gen, device="cuda", dtype=torch.int8)
         else:
             codes = (torch.randint(0, 2, (p.N, p.K), generator=gen, device="cuda", dtype=torch.int8) * 2 - 1)
         words, _ = lb.pack(codes.contiguous(), p.bits, count_invalid=False)
@@ -169,7 +184,7 @@ def make_device_inputs(probs, seed):
         y = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
         bufs.append((x, words, s, y, p.g, p.bits))
     torch.cuda.synchronize()
-    return bufs
+    return bufs, biases
 
 
 def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=False):
@@ -187,9 +202,9 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=Fal
     cases = []
     for (N, K, bits, g), p in seen.items():
         m = p.M if rows <= 0 else min(rows, p.M)
-        q = W.Problem(p.name, m, N, K, bits, g, p.config_id, p.tensor_id)
+        q = W.Problem(p.name, m, N, K, bits, g, p.config_id, p.tensor_id, affine=p.affine)
         inp = W.make_inputs(q, seed)
-        words, _ = oracle.pack(inp.codes, bits)
+        words, _ = oracle.pack_u4(inp.codes) if q.affine else oracle.pack(inp.codes, bits)
         cases.append((q, inp, words))
     # whole passes over the sample until at least `min_seconds` of oracle time
     flops = nbytes = passes = 0
@@ -199,6 +214,8 @@ def cpu_baseline(probs, rows, seed, unit="TFLOP/s", min_seconds=10.0, swiglu=Fal
             t0 = time.perf_counter()
             if swiglu:
                 oracle.swiglu_ref_f64(inp.x, oracle.unpack(words, q.K, q.bits), inp.scales, q.g)
+            elif q.affine:
+                oracle.gemm_affine_ref_f64(inp.x, oracle.unpack_u4(words, q.K), inp.scales, inp.biases, q.g)
             else:
                 oracle.gemm_ref_from_words(inp.x, words, inp.scales, q.K, q.g, q.bits)
             elapsed += time.perf_counter() - t0
@@ -265,7 +282,7 @@ def main():
     import workloads as W
     probs = problems_for(a.workload)
     groups = W.step_groups(probs) if a.workload in ("sweep", "skinny") else [[i] for i in range(len(probs))]
-    bufs = make_device_inputs(probs, a.seed)
+    bufs, biases = make_device_inputs(probs, a.seed)
     swiglu = a.workload in ("swiglu", "swiglu16")
     residual = a.workload == "residual"
     if residual:  # residual stream R (N(0,1)) and a per-feature gate, drawn once
@@ -296,6 +313,9 @@ def main():
         elif residual:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm_residual(x, w, s, g, bits, res_r, res_g, out=y)
+        elif len(grp) == 1 and grp[0] in biases:
+            x, w, s, y, g, bits = bufs[grp[0]]
+            lb.gemm_affine(x, w, s, biases[grp[0]], g, out=y)
         elif len(grp) == 1:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm(x, w, s, g, bits, out=y, workspace=ws)

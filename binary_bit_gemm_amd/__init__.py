@@ -75,6 +75,48 @@ def pack(codes, bits: int, count_invalid: bool = True) -> Tuple["object", Option
     return words, (int(bad.item()) if bad is not None else None)
 
 
+def pack_u4(levels, count_invalid: bool = True):
+    """Unsigned 4-bit levels (uint8 [N, K], 0 .. 15) on the GPU -> (packed words [N, K/8] as
+    int32, invalid count) for lowbit_gemm_affine (lowbit_pack_u4)."""
+    torch = _torch()
+    _require(levels, torch.uint8, "levels")
+    N, K = levels.shape
+    words = torch.empty((N, K // 8), dtype=torch.int32, device=levels.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=levels.device) if count_invalid else None
+    st = lib().lowbit_pack_u4(ctypes.c_void_p(levels.data_ptr()), ctypes.c_void_p(words.data_ptr()), N, K,
+                              ctypes.c_void_p(bad.data_ptr() if bad is not None else 0),
+                              ctypes.c_void_p(_stream_ptr(levels.device)))
+    _check(st, "lowbit_pack_u4")
+    return words, (int(bad.item()) if bad is not None else None)
+
+
+def gemm_affine(x, words, scales, biases, g: int, out=None):
+    """Y = X . W^T with affine 4-bit groups W = S * q + B (lowbit_gemm_affine): `words` from
+    pack_u4, `scales` and `biases` fp16 [N, K/g]."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    _require(words, torch.int32, "words")
+    _require(scales, torch.float16, "scales")
+    _require(biases, torch.float16, "biases")
+    M, K = x.shape
+    N = words.shape[0]
+    if words.shape[1] != K // 8 or K % 8:
+        raise ValueError(f"words must be [N, K/8] = [{N}, {K // 8}], got {tuple(words.shape)}")
+    if K % g or tuple(scales.shape) != (N, K // g) or tuple(biases.shape) != (N, K // g):
+        raise ValueError(f"scales and biases must be [N, K/g] = [{N}, {K // g if g else 0}]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().lowbit_gemm_affine(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(biases.data_ptr()),
+                                  ctypes.c_void_p(out.data_ptr()), M, N, K, g, ctypes.c_void_p(_stream_ptr(x.device)))
+    _check(st, "lowbit_gemm_affine")
+    return out
+
+
 def unpack(words, K: int, bits: int):
     """Packed words [N, K*bits/32] -> int8 codes [N, K]."""
     torch = _torch()

@@ -13,6 +13,8 @@ _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "lowbit_pack": (_INT, [_VP, _VP, _I64, _I64, _INT, _VP, _VP]),
     "lowbit_unpack": (_INT, [_VP, _VP, _I64, _I64, _INT, _VP]),
+    "lowbit_pack_u4": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP]),
+    "lowbit_gemm_affine": (_INT, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
     "lowbit_import_ternary": (_INT, [_VP, _INT, _INT, _VP, _I64, _I64, _VP, _VP]),
     "lowbit_import_binary_gemlite": (_INT, [_VP, _VP, _I64, _I64, _VP]),
     "lowbit_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),

@@ -76,9 +76,17 @@ struct Cfg16 {
 // output columns, so the epilogue combines them in registers; a BN-row weight tile makes BN / 2
 // output columns.  EPI = kEpiResidual: Y = R + gate[n] * (X . W^T) in fp32, rounded once (Y may
 // be R: every element is read and written by the same lane).
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int EPI = kEpiPlain>
+// AFFINE (4-bit codes only): the nibbles are unsigned levels q of affine groups, w = s * q + b with
+// an fp16 scale S and an fp16 bias B per group (the 4-bit text encoder's bits = 4, group_size = 64
+// quantisation of the mlx guide's component architecture).  Per group the output gains
+// b * (sum of the group's activations); that row sum comes from one MFMA pair against an all-ones
+// operand per row block (exact products, fp32 sums, in the accumulator layout), shared by the
+// wave's column blocks, and enters with one more fp32 FMA per output and group.
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int EPI = kEpiPlain,
+          bool AFFINE = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp) {
     constexpr bool SWIGLU = EPI == kEpiSwiglu;
+    static_assert(!AFFINE || (BITS == 4 && EPI == kEpiPlain), "affine groups: 4-bit levels, plain epilogue");
     using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
     constexpr int kWSpb = C::W_SPB;
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && C::WAVES == 4), "K groups of 4 waves, two of them");
@@ -93,6 +101,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     __shared__ __attribute__((aligned(16))) unsigned char wk1_[KSPLIT][C::W_BLOCK];
     __shared__ __attribute__((aligned(16))) unsigned char sk0_[KSPLIT][C::S_BLOCK];
     __shared__ __attribute__((aligned(16))) unsigned char sk1_[KSPLIT][C::S_BLOCK];
+    // affine groups: the bias blocks, laid out as the scale blocks
+    constexpr int kBBlock = AFFINE ? C::S_BLOCK : 16;
+    __shared__ __attribute__((aligned(16))) unsigned char bk0_[KSPLIT][kBBlock];
+    __shared__ __attribute__((aligned(16))) unsigned char bk1_[KSPLIT][kBBlock];
 
     // K group kg (wave-uniform) and the thread's index inside it
     const int kg = KSPLIT == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) / C::THREADS);
@@ -102,6 +114,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     unsigned char* const wk1 = wk1_[kg];
     unsigned char* const sk0 = sk0_[kg];
     unsigned char* const sk1 = sk1_[kg];
+    unsigned char* const bk0 = bk0_[kg];
+    unsigned char* const bk1 = bk1_[kg];
     const int tid = int(threadIdx.x) - kg * C::THREADS;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     // valid row; their results are not stored).  SwiGLU: row r = 32 w + 16 h + i is output
     // column n0 + 16 w + i, of the gate (h = 0) or the up (h = 1) half.
     const int w_rows = SWIGLU ? 2 * N : N;
-    auto wrow = [&](int r) {
+    auto wrow = [&](int r) __attribute__((always_inline)) {
         if constexpr (SWIGLU) {
             const int c = n0 + 16 * (r >> 5) + (r & 15);
             return (c < N ? c : N - 1) + ((r >> 4) & 1) * N;
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     const uint32_t x_row_step = uint32_t(kRowsPerRound) * uint32_t(K) * 2u;
     const unsigned char* x_tile = reinterpret_cast<const unsigned char*>(p.X) + size_t(m0) * size_t(K) * 2;
     const uint32_t x_tile_bytes = uint32_t(M - m0 < BM ? M - m0 : BM) * uint32_t(K) * 2u;
-    auto issue_x = [&](int step, unsigned char* buf) {
+    auto issue_x = [&](int step, unsigned char* buf) __attribute__((always_inline)) {
         const uint32_t kb = uint32_t(step) * KS * 2u;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(x_tile + kb, x_tile_bytes - kb);
 #pragma unroll
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     // Copy slot s = row s / 4, stored position s % 4 (holding source chunk w_pos(row, s % 4)).
     // Rows past N re-read row N-1.
     const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(p.W, uint32_t(w_rows) * w_row_bytes);
-    auto issue_w = [&](int block, unsigned char* buf) {
+    auto issue_w = [&](int block, unsigned char* buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < (C::W_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
             const int slot0 = i * C::THREADS + wave_u * 64;
@@ -180,7 +194,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     // ---- scales: block b = groups [8b, 8b+8) of the tile's BN rows, as two aligned 16-byte
     // windows per row; the row's group 8b sits (row offset & 15) bytes in.
     const __amdgpu_buffer_rsrc_t s_rs = make_rsrc(p.S, uint32_t(w_rows) * s_row_bytes);
-    auto issue_s = [&](int block, unsigned char* buf) {
+    const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(AFFINE ? p.B : p.S, uint32_t(w_rows) * s_row_bytes);
+    // scale block `block` into `buf` (affine: the bias block alike into `bbuf`)
+    auto issue_s = [&](int block, unsigned char* buf, unsigned char* bbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < (C::S_SLOTS + C::THREADS - 1) / C::THREADS; ++i) {
             const int slot0 = i * C::THREADS + wave_u * 64;
@@ -191,6 +207,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
                 const uint32_t start = uint32_t(n) * s_row_bytes + uint32_t(block) * 16u;
                 const uint32_t voff = (start & ~15u) + uint32_t(slot & 1) * 16u;
                 dma16(s_rs, buf + slot0 * 16, voff, 0);
+                if constexpr (AFFINE) dma16(b_rs, bbuf + slot0 * 16, voff, 0);
             }
         }
     };
@@ -228,8 +245,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     struct Ops {
         u32x2_t w[C::NB];
         float sc[C::NB];
+        float bs[AFFINE ? C::NB : 1];  // affine: the group's bias
     };
-    auto read_operands = [&](const unsigned char* wt, const unsigned char* st, int step, Ops& o) {
+    auto read_operands = [&](const unsigned char* wt, const unsigned char* st, const unsigned char* bt, int step,
+                             Ops& o) __attribute__((always_inline)) {
         const int wj = step % kWSpb;
         const int grp_in_block = (step * KS / G) & (kSGpb - 1);
 #pragma unroll
@@ -251,18 +270,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             // across the unrolled steps).
             o.sc[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(st + s_rd[nb] + grp_in_block * 2)) *
                        (BITS == 2 ? 0.5f : BITS == 4 ? 0.0625f : -0.5f);
+            if constexpr (AFFINE)
+                o.bs[nb] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(bt + s_rd[nb] + grp_in_block * 2));
         }
     };
 
-    auto compute = [&](const unsigned char* xt, const Ops& o) {
+    auto compute = [&](const unsigned char* xt, const Ops& o) __attribute__((always_inline)) {
         // Codes of column block nb are expanded just before its first MFMA pair (row block 0),
         // behind a scheduling fence: the expansion of block nb + 1 then runs while the matrix
         // core works on block nb, instead of every wave of a SIMD expanding all its codes
         // right after the step's barrier while the matrix core idles.
         u32x4_t bfr[C::NB][2];
-        auto expand = [&](int nb) {
+        auto expand = [&](int nb) __attribute__((always_inline)) {
             uint32_t d[8];
-            if constexpr (BITS == 4) {
+            if constexpr (AFFINE) {
+                expand_u4_word(o.w[nb][0], d);
+                expand_u4_word(o.w[nb][1], d + 4);
+            } else if constexpr (BITS == 4) {
                 expand_int4_word(o.w[nb][0], d);
                 expand_int4_word(o.w[nb][1], d + 4);
             } else {
@@ -282,6 +306,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         // depend on mb: one base address per chunk, the row block as an immediate offset.
         f32x4_t tmp[2];
         bf16x8_t afr[2][2];  // [row block parity][k half]
+        // affine: the row block's activation sums over the step (rows 4q + i in lane (q, l16),
+        // every column alike), from an MFMA pair against an all-ones operand
+        f32x4_t rsum[2];
+        const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
         for (int j = 0; j < 2; ++j) afr[0][j] = *reinterpret_cast<const bf16x8_t*>(xt + x_rd[j]);
         int pb = -1;  // previous block, its partial sum in tmp[pb & 1]
@@ -291,6 +319,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     afr[(mb + 1) & 1][j] = *reinterpret_cast<const bf16x8_t*>(xt + x_rd[j] + (mb + 1) * 16 * kRowBytes);
+            }
+            if constexpr (AFFINE) {
+                f32x4_t r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 2; ++j) r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mb & 1][j], ones, r, 0, 0, 0);
+                rsum[mb & 1] = r;
             }
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
@@ -307,6 +341,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
                     const int pm = pb / C::NB, pn = pb % C::NB;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[pm][pn][i] = __builtin_fmaf(o.sc[pn], tmp[pb & 1][i], acc[pm][pn][i]);
+                    if constexpr (AFFINE) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[pm][pn][i] = __builtin_fmaf(o.bs[pn], rsum[pm & 1][i], acc[pm][pn][i]);
+                    }
                 }
                 pb = b;
             }
@@ -315,6 +354,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             const int pm = pb / C::NB, pn = pb % C::NB;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[pm][pn][i] = __builtin_fmaf(o.sc[pn], tmp[pb & 1][i], acc[pm][pn][i]);
+            if constexpr (AFFINE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[pm][pn][i] = __builtin_fmaf(o.bs[pn], rsum[pm & 1][i], acc[pm][pn][i]);
+            }
         }
         // An empty side-effecting use of every accumulator closes the step: otherwise the
         // compiler sinks this step's scale FMAs past the barrier into the next step's first
@@ -325,29 +368,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             for (int nb = 0; nb < C::NB; ++nb) asm volatile("" ::"v"(acc[mb][nb]));
     };
 
-    auto w_buf = [&](int step) -> unsigned char* { return ((step / kWSpb) & 1) ? wk1 : wk0; };
-    auto s_block = [&](int step) { return (step * KS / G) / kSGpb; };
-    auto s_buf = [&](int step) -> unsigned char* { return (s_block(step) & 1) ? sk1 : sk0; };
+    auto w_buf = [&](int step) __attribute__((always_inline)) -> unsigned char* { return ((step / kWSpb) & 1) ? wk1 : wk0; };
+    auto s_block = [&](int step) __attribute__((always_inline)) { return (step * KS / G) / kSGpb; };
+    auto s_buf = [&](int step) __attribute__((always_inline)) -> unsigned char* { return (s_block(step) & 1) ? sk1 : sk0; };
+    auto b_buf = [&](int step) __attribute__((always_inline)) -> unsigned char* { return (s_block(step) & 1) ? bk1 : bk0; };
     const int w_blocks = (ksteps + kWSpb - 1) / kWSpb;
     const int s_blocks = (kgroups + kSGpb - 1) / kSGpb;
 
-    auto prefetch_x = [&](int step, unsigned char* xbuf) {
+    auto prefetch_x = [&](int step, unsigned char* xbuf) __attribute__((always_inline)) {
         if (step + 1 < kend) issue_x(step + 1, xbuf);
     };
     // The next weight (scale) block is copied on the first step of a block and on the group's
     // first step, which can fall inside a block.
-    auto prefetch_blocks = [&](int step) {
+    auto prefetch_blocks = [&](int step) __attribute__((always_inline)) {
         const int wb = step / kWSpb;
         if ((step == kbeg || step % kWSpb == 0) && wb + 1 < w_blocks && (wb + 1) * kWSpb < kend)
             issue_w(wb + 1, ((wb + 1) & 1) ? wk1 : wk0);
         const int sb = s_block(step);
-        if ((step == kbeg || s_block(step - 1) != sb) && sb + 1 < s_blocks && s_block(kend - 1) > sb)
-            issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+        if ((step == kbeg || s_block(step - 1) != sb) && sb + 1 < s_blocks && s_block(kend - 1) > sb) {
+            if constexpr (AFFINE)
+                issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0, ((sb + 1) & 1) ? bk1 : bk0);
+            else
+                issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0, nullptr);
+        }
     };
 
     issue_x(kbeg, xa0);
     issue_w(kbeg / kWSpb, w_buf(kbeg));
-    issue_s(s_block(kbeg), s_buf(kbeg));
+    issue_s(s_block(kbeg), s_buf(kbeg), AFFINE ? b_buf(kbeg) : nullptr);
     wait_vmcnt0();
     __syncthreads();
 
@@ -359,13 +407,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     int step = kbeg;
 #pragma nounroll
     for (; step + 1 < kend; step += 2) {
-        read_operands(w_buf(step), s_buf(step), step, ops);
+        read_operands(w_buf(step), s_buf(step), AFFINE ? b_buf(step) : nullptr, step, ops);
         prefetch_x(step, xa1);
         prefetch_blocks(step);
         compute(xa0, ops);
         wait_vmcnt0();
         __syncthreads();
-        read_operands(w_buf(step + 1), s_buf(step + 1), step + 1, ops);
+        read_operands(w_buf(step + 1), s_buf(step + 1), AFFINE ? b_buf(step + 1) : nullptr, step + 1, ops);
         prefetch_x(step + 1, xa0);
         prefetch_blocks(step + 1);
         compute(xa1, ops);
@@ -373,7 +421,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         __syncthreads();
     }
     if (step < kend) {
-        read_operands(w_buf(step), s_buf(step), step, ops);
+        read_operands(w_buf(step), s_buf(step), AFFINE ? b_buf(step) : nullptr, step, ops);
         compute(xa0, ops);
     }
 
@@ -387,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         static_assert(C::X_TILE == C::W_BLOCK && C::MB * C::NB <= 2 * kPer, "a wave's sums fit two buffers");
         unsigned char* const r0 = wave_u == 0 ? xa0_[0] : wave_u == 1 ? xa1_[0] : wave_u == 2 ? wk0_[0] : wk1_[0];
         unsigned char* const r1 = wave_u == 0 ? xa0_[1] : wave_u == 1 ? xa1_[1] : wave_u == 2 ? wk0_[1] : wk1_[1];
-        auto slot = [&](int b) {
+        auto slot = [&](int b) __attribute__((always_inline)) {
             return reinterpret_cast<f32x4_t*>(b < kPer ? r0 + 1024 * b : r1 + 1024 * (b - kPer)) + lane;
         };
         if (kg == 1) {
@@ -425,11 +473,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     const uint32_t d1_sel = odd ? 0x03020706u : 0x07060100u;     // (R.hi, F.hi) : (F.lo, R.hi)
     constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
     constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-    auto pack = [](float lo, float hi) {
+    auto pack = [](float lo, float hi) __attribute__((always_inline)) {
         return uint32_t(float_to_bf16_bits(lo)) | (uint32_t(float_to_bf16_bits(hi)) << 16);
     };
     // one 16x16 block of fp32 results to bf16 at columns nblk .. nblk + 15 of row block mb
-    auto store_block = [&](f32x4_t a, int nblk, int mb) {
+    auto store_block = [&](f32x4_t a, int nblk, int mb) __attribute__((always_inline)) {
         if (nblk >= N) return;  // N % 16 == 0: a block is in or out as a whole
         if constexpr (EPI == kEpiResidual) {
             // lane (q, l16) holds column nblk + l16 of rows 4q + i: the gated residual update
@@ -475,7 +523,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     }
 }
 
-template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, int EPI = kEpiPlain>
+template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, int EPI = kEpiPlain,
+          bool AFFINE = false>
 hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
     ProblemGroup grp{};
     int total = 0;
@@ -486,7 +535,7 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
         grp.tile_end[i] = total;
     }
     grp.count = count;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI>), dim3(total),
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI, AFFINE>), dim3(total),
                        dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
     return hipGetLastError();
 }
@@ -495,7 +544,7 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
 
 bool tile16_supported(int g, int bits) { return (bits == 1 || bits == 2 || bits == 4) && (g == 64 || g == 128); }
 
-template <int G, int BITS>
+template <int G, int BITS, bool AFFINE = false>
 hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hipStream_t stream) {
     // 288 x 192 in 12 waves of 144 x 32: LDS 72 KB (X) + 24 KB (W) + 12 KB (S).  The step is
     // bound by VALU issue (code expansion and scale FMAs next to the MFMAs); 144 x 32 wave tiles
@@ -509,18 +558,18 @@ hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hi
         if (variant == TILE_64x128K2) {
             bool even = true;
             for (int i = 0; i < count; ++i) even = even && (probs[i].K / KS) % 2 == 0;
-            if (even) return launch_cfg16<G, BITS, 64, 128, 1, 4, 2>(probs, count, stream);
-            return launch_cfg16<G, BITS, 64, 128, 1, 4>(probs, count, stream);
+            if (even) return launch_cfg16<G, BITS, 64, 128, 1, 4, 2, kEpiPlain, AFFINE>(probs, count, stream);
+            return launch_cfg16<G, BITS, 64, 128, 1, 4, 1, kEpiPlain, AFFINE>(probs, count, stream);
         }
     }
     if (variant == TILE_96x192K2) {
         bool even = true;
         for (int i = 0; i < count; ++i) even = even && (probs[i].K / KS) % 2 == 0;
-        if (even) return launch_cfg16<G, BITS, 96, 192, 1, 4, 2>(probs, count, stream);
-        return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
+        if (even) return launch_cfg16<G, BITS, 96, 192, 1, 4, 2, kEpiPlain, AFFINE>(probs, count, stream);
+        return launch_cfg16<G, BITS, 96, 192, 1, 4, 1, kEpiPlain, AFFINE>(probs, count, stream);
     }
-    if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4>(probs, count, stream);
-    return launch_cfg16<G, BITS, 288, 192, 2, 6>(probs, count, stream);
+    if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4, 1, kEpiPlain, AFFINE>(probs, count, stream);
+    return launch_cfg16<G, BITS, 288, 192, 2, 6, 1, kEpiPlain, AFFINE>(probs, count, stream);
 }
 
 template <int G, int BITS, int EPI>
@@ -543,6 +592,13 @@ hipError_t launch_gemm_tile16_epilogue(const GemmProblem* probs, int count, int 
     if (epi == kEpiSwiglu) return launch_epi16_gb<kEpiSwiglu>(probs, count, g, bits, stream);
     if (epi == kEpiResidual) return launch_epi16_gb<kEpiResidual>(probs, count, g, bits, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_tile16_affine(const GemmProblem* probs, int count, int g, int variant, hipStream_t stream) {
+    if (count < 1 || count > kMaxGroup || !tile16_supported(g, 4)) return hipErrorInvalidValue;
+    if (!is_tile16_variant(variant)) variant = TILE_288x192;
+    return g == 64 ? launch_variant16<64, 4, true>(probs, count, variant, stream)
+                   : launch_variant16<128, 4, true>(probs, count, variant, stream);
 }
 
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,

@@ -272,6 +272,40 @@ int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 
+int lowbit_pack_u4(const uint8_t* levels, uint32_t* W, int64_t N, int64_t K, int32_t* bad_count, void* stream) {
+    int st = check_pack_args(levels, W, N, K, 4);
+    if (st != LOWBIT_OK || N * K == 0) return st;
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    hipError_t e = lowbit::launch_pack_u4(levels, W, N, K, bad_count, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
+int lowbit_gemm_affine(const void* X, const uint32_t* W, const void* S, const void* B, void* Y, int64_t M,
+                       int64_t N, int64_t K, int g, void* stream) {
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, 4);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    if (K > 0 && B == nullptr) return LOWBIT_E_INVALID;
+    if (K > 0 && !aligned16(B)) return LOWBIT_E_ALIGN;
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                          static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
+    p.B = static_cast<const uint16_t*>(B);
+    hipError_t e;
+    if (K == 0) {  // an empty sum
+        const int64_t n = M * N;
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p.Y, n);
+        e = hipGetLastError();
+    } else {
+        const int f = forced_variant();
+        const int v = f >= 0 && f < 100 ? f : lowbit::pick_tile_variant(M, N, K, g, 4);
+        e = lowbit::launch_gemm_tile16_affine(&p, 1, g, v, s);
+    }
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
 int lowbit_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits, void* stream) {
     int st = check_pack_args(codes, W, N, K, bits);
     if (st != LOWBIT_OK || N * K == 0) return st;

@@ -49,6 +49,21 @@ __device__ __forceinline__ void expand_int4_word(uint32_t w, uint32_t out[4]) {
     }
 }
 
+// 8 unsigned 4-bit levels (level i at bits 4i .. 4i+3) -> 8 bf16 of 16 * level, paired as in
+// expand_int4_word.  Each level moves to the top nibble of a byte, whose unsigned value is
+// 16 * level (0 .. 240); its fp32 conversion is exact, and so is the bf16 taken as the upper half
+// of that fp32 (at most 4 significant bits).
+__device__ __forceinline__ void expand_u4_word(uint32_t w, uint32_t out[4]) {
+    const uint32_t ev = (w << 4) & 0xF0F0F0F0u;  // levels 0, 2, 4, 6
+    const uint32_t od = w & 0xF0F0F0F0u;         // levels 1, 3, 5, 7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float fe = static_cast<float>(static_cast<uint8_t>(ev >> (8 * j)));
+        const float fo = static_cast<float>(static_cast<uint8_t>(od >> (8 * j)));
+        out[j] = perm_b32(__float_as_uint(fo), __float_as_uint(fe), 0x07060302u);
+    }
+}
+
 __device__ __forceinline__ void expand_ternary_word(uint32_t w, uint32_t out[8]) {
     constexpr uint32_t kHighByte = 0x00C04000u;
     const uint32_t e0 = w & 0x03030303u;

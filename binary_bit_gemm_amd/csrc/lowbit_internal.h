@@ -15,6 +15,7 @@ struct GemmProblem {
     int M, N, K;
     const uint16_t* R = nullptr;     // gated-residual epilogue only: bf16 residual [M, N] (may be Y)
     const uint16_t* gate = nullptr;  // gated-residual epilogue only: bf16 gate [N]
+    const uint16_t* B = nullptr;     // affine 4-bit groups only: fp16 biases [N, K/g]
 };
 
 // Epilogues of the 16x16-block tile kernel and of the resident kernel.
@@ -35,6 +36,9 @@ struct ProblemGroup {
 
 hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
                        int32_t* bad_count, hipStream_t stream);
+// Unsigned 4-bit levels 0 .. 15 -> nibble words (levels above 15 pack as 0 and are counted).
+hipError_t launch_pack_u4(const uint8_t* levels, uint32_t* W, int64_t N, int64_t K, int32_t* bad_count,
+                          hipStream_t stream);
 hipError_t launch_unpack(const uint32_t* W, int8_t* codes, int64_t N, int64_t K, int bits,
                          hipStream_t stream);
 // Ternary importers (import.hip): the layouts of include/lowbit.h's LOWBIT_LAYOUT_* values.
@@ -104,6 +108,9 @@ hipError_t launch_gemm_tile16_epilogue(const GemmProblem* probs, int count, int 
                                        hipStream_t stream);
 hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                     hipStream_t stream);
+// Affine 4-bit groups (unsigned levels, w = s * q + b with each problem's B set) on a 16x16-block
+// tile; `variant` as for 4-bit codes.
+hipError_t launch_gemm_tile16_affine(const GemmProblem* probs, int count, int g, int variant, hipStream_t stream);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit

@@ -2,8 +2,8 @@
 //
 // One thread per output uint32 word.  Ternary: 16 int8 codes -> 2-bit fields
 // (00 -> 0, 01 -> +1, 10 -> -1), binary: 32 codes -> bits (1 -> +1, 0 -> -1), 4-bit: 8 codes
-// in [-8, 7] -> two's complement nibbles; least significant field first along K.  Invalid
-// codes pack as 0 bits and are counted.
+// in [-8, 7] -> two's complement nibbles, affine 4-bit: 8 unsigned levels 0 .. 15 -> nibbles;
+// least significant field first along K.  Invalid codes pack as 0 bits and are counted.
 #include "lowbit_internal.h"
 
 namespace lowbit {
@@ -74,6 +74,33 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* __restrict
     }
 }
 
+// Unsigned 4-bit levels of affine groups: 8 levels 0 .. 15 -> nibbles, least significant first.
+__global__ __launch_bounds__(kThreads) void pack_u4_kernel(const uint8_t* __restrict__ levels,
+                                                           uint32_t* __restrict__ W, int64_t nwords,
+                                                           int32_t* __restrict__ bad_count) {
+    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    int bad = 0;
+    if (i < nwords) {
+        const uint2 v = *reinterpret_cast<const uint2*>(levels + i * 8);
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t q = ((k < 4 ? v.x : v.y) >> (8 * (k & 3))) & 0xFFu;
+            bad += q > 15u;
+            word |= (q <= 15u ? q : 0u) << (4 * k);
+        }
+        W[i] = word;
+    }
+    if (bad_count != nullptr) {
+        const unsigned long long mask = __ballot(bad != 0);
+        if (mask != 0) {
+            int total = bad;
+            for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+            if ((threadIdx.x & 63) == 0) atomicAdd(bad_count, total);
+        }
+    }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __restrict__ W,
                                                           int8_t* __restrict__ codes, int64_t nwords) {
@@ -129,6 +156,15 @@ hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, i
         hipLaunchKernelGGL(pack_kernel<2>, grid, dim3(kThreads), 0, stream, codes, W, nwords, bad_count);
     else
         hipLaunchKernelGGL(pack_kernel<1>, grid, dim3(kThreads), 0, stream, codes, W, nwords, bad_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_u4(const uint8_t* levels, uint32_t* W, int64_t N, int64_t K, int32_t* bad_count,
+                          hipStream_t stream) {
+    const int64_t nwords = N * K / 8;
+    if (nwords == 0) return hipSuccess;
+    const dim3 grid(unsigned((nwords + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(pack_u4_kernel, grid, dim3(kThreads), 0, stream, levels, W, nwords, bad_count);
     return hipGetLastError();
 }
 

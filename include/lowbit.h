@@ -26,9 +26,10 @@
  *   binary  (bits = 1): 32 codes per uint32, along K: code k of row n is bit k%32 of
  *       W[n * (K/32) + k/32];  1 -> +1, 0 -> -1.
  *   4-bit   (bits = 4): 8 codes per uint32, along K: code k of row n is the two's complement
- *       nibble at bits 4*(k%8) .. 4*(k%8)+3 of W[n * (K/8) + k/8], values -8 .. 7 (the 4-bit
- *       text encoder of the binary model card's "Model Overview" table; the card gives no
- *       zero point, so the form is the same symmetric w = s * c).
+ *       nibble at bits 4*(k%8) .. 4*(k%8)+3 of W[n * (K/8) + k/8], values -8 .. 7, symmetric
+ *       w = s * c (the 4-bit text encoder of the binary model card's "Model Overview" table).
+ *       The affine form of the same encoder (unsigned levels with a scale and a bias per
+ *       group) has its own entry points: lowbit_pack_u4 and lowbit_gemm_affine.
  *   scales: fp16 (IEEE binary16) S[n * (K/g) + k/g], symmetric (no zero point).
  * Activations X[M, K] and outputs Y[M, N] are bf16, row-major, contiguous.
  *
@@ -83,6 +84,19 @@ enum {
  */
 int lowbit_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
                 int32_t* bad_count, void* stream);
+
+/*
+ * lowbit_pack_u4 -- unsigned 4-bit levels [N, K] -> packed words [N, K/8] for affine groups
+ * (lowbit_gemm_affine): level k of row n is the nibble at bits 4*(k%8) .. 4*(k%8)+3 of
+ * W[n * (K/8) + k/8] (least significant nibble first, the same positions as the signed 4-bit
+ * format).
+ *   levels     device, N*K uint8 in 0 .. 15, row-major.
+ *   W          device, N*K/8 uint32, written.
+ *   bad_count  device int32 or NULL: levels above 15 pack as 0 and their number is ADDED to
+ *              *bad_count (the caller zeroes it).
+ *   Requires K % 8 == 0; errors as lowbit_pack.  Offline, load-time step.
+ */
+int lowbit_pack_u4(const uint8_t* levels, uint32_t* W, int64_t N, int64_t K, int32_t* bad_count, void* stream);
 
 /*
  * lowbit_unpack -- packed words -> int8 codes [N, K] (ternary field 11 -> 0).
@@ -258,6 +272,23 @@ int lowbit_gemm_swiglu(const void* X, const uint32_t* W, const void* S, void* Y,
  */
 int lowbit_gemm_residual(const void* X, const uint32_t* W, const void* S, const void* R, const void* gate,
                          void* Y, int64_t M, int64_t N, int64_t K, int g, int bits, void* stream);
+
+/*
+ * lowbit_gemm_affine -- Y[M, N] = X[M, K] . W[N, K]^T for 4-bit weights in affine groups,
+ *     W[n, k] = S[n, k/g] * q[n, k] + B[n, k/g],   q in 0 .. 15 unsigned,
+ * the form of the text encoder that the mlx guide's component architecture loads quantised at
+ * bits = 4, group_size = 64 (MLX's affine 4-bit groups; an HQQ zero point z is B = -z * S).
+ *   X  device bf16 [M, K];  W  device packed levels [N, K/8] (lowbit_pack_u4);
+ *   S, B  device fp16 [N, K/g] scales and biases;  Y  device bf16 [M, N], fully overwritten.
+ * The levels are expanded to bf16 (exact) and multiplied on the bf16 matrix cores with fp32
+ * sums; per group the fp32 sum times S, plus B times the group's fp32 activation sum (from the
+ * matrix cores against an all-ones operand), is added in fp32; Y is rounded to bf16 once.
+ * g = 64 or 128 (g = 32 returns LOWBIT_E_UNSUPPORTED).  A null or unaligned B with K > 0 returns
+ * LOWBIT_E_INVALID / LOWBIT_E_ALIGN; other checks as lowbit_gemm with bits = 4.  K = 0 gives
+ * Y = 0.  Runs on the 16x16-block tile kernel at every M.
+ */
+int lowbit_gemm_affine(const void* X, const uint32_t* W, const void* S, const void* B, void* Y,
+                       int64_t M, int64_t N, int64_t K, int g, void* stream);
 
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */

@@ -18,7 +18,7 @@ OK, INVALID, UNSUPPORTED, ALIGN, HIP, TOO_MANY = 0, 1, 2, 3, 4, 5
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lowbit_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lowbit_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -264,3 +264,19 @@ def test_noalloc_validates_before_the_device(monkeypatch):
     monkeypatch.setenv("LOWBIT_RESIDENT_PLAN", "1,16")
     assert lb.workspace_size(16, 16384, 16384, 64, 2) > lb.NOALLOC_SCRATCH_BYTES
     assert L.lowbit_gemm_noalloc(A, A, A, A, 16, 16384, 16384, 64, 2, None) == SCRATCH
+
+
+def test_affine_entry_points_validate_before_the_device():
+    L = lb.lib()
+    A = 256
+    # lowbit_pack_u4: K % 8, alignment, nulls
+    assert L.lowbit_pack_u4(A, A, 16, 12, None, None) == INVALID
+    assert L.lowbit_pack_u4(A + 4, A, 16, 64, None, None) == ALIGN
+    assert L.lowbit_pack_u4(None, A, 16, 64, None, None) == INVALID
+    assert L.lowbit_pack_u4(None, None, 0, 64, None, None) == OK
+    # lowbit_gemm_affine: 4-bit rules (g = 32 unsupported), the bias pointer checked like the others
+    assert L.lowbit_gemm_affine(A, A, A, A, A, 16, 256, 256, 32, None) == UNSUPPORTED
+    assert L.lowbit_gemm_affine(A, A, A, None, A, 16, 256, 256, 64, None) == INVALID
+    assert L.lowbit_gemm_affine(A, A, A, A + 2, A, 16, 256, 256, 64, None) == ALIGN
+    assert L.lowbit_gemm_affine(A, A, A, A, A, 16, 250, 256, 64, None) == INVALID
+    assert L.lowbit_gemm_affine(A, A, A, A, A, 0, 256, 256, 64, None) == OK
