@@ -369,7 +369,14 @@ hipError_t launch_cfg(const ResidentArgs& a, uint32_t lds, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemm_resident_kernel<G, LEN, EPI>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds,
                        stream, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && trace_enabled()) {
+        char cfg[96];
+        snprintf(cfg, sizeof cfg, "column_blocks=%d k_slices=%d steps=%d splits=%d tiles=%d epi=%s", a.cb, a.ks, LEN,
+                 a.splits, a.tiles, EPI == kEpiSwiglu ? "swiglu" : EPI == kEpiResidual ? "residual" : "plain");
+        trace_launch("resident", cfg, G, 2, a.grp.p, a.grp.count, unsigned(a.tiles * a.splits), 64u * a.cb * a.ks, lds);
+    }
+    return e;
 }
 
 template <int G, int EPI = kEpiPlain>

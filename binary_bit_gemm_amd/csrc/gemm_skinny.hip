@@ -328,7 +328,13 @@ hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
     }
     grp.count = count;
     hipLaunchKernelGGL((gemm_skinny_kernel<BITS, G, MB, NCB, WAVES>), dim3(total), dim3(64 * WAVES), 0, stream, grp);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && trace_enabled()) {
+        char cfg[64];
+        snprintf(cfg, sizeof cfg, "row_blocks=%d column_blocks=%d waves=%d", MB, NCB, WAVES);
+        trace_launch("skinny", cfg, G, BITS, probs, count, unsigned(total), 64u * WAVES, 0u);
+    }
+    return e;
 }
 
 // Wider stripes only where the registers allow them: four column blocks for one row block of

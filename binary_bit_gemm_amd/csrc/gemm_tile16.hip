@@ -537,7 +537,14 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
     grp.count = count;
     hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI, AFFINE>), dim3(total),
                        dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && trace_enabled()) {
+        char cfg[96];
+        snprintf(cfg, sizeof cfg, "%dx%d waves=%dx%dx%d epi=%s%s", BM, BN, WAVES_M, WAVES_N, KSPLIT,
+                 EPI == kEpiSwiglu ? "swiglu" : EPI == kEpiResidual ? "residual" : "plain", AFFINE ? " affine" : "");
+        trace_launch("tile16", cfg, G, BITS, probs, count, unsigned(total), 64u * WAVES_M * WAVES_N * KSPLIT, 0u);
+    }
+    return e;
 }
 
 }  // namespace

@@ -345,7 +345,13 @@ hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
     grp.count = count;
     hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>), dim3(total),
                        dim3(64 * WAVES_M * WAVES_N), 0, stream, grp);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && trace_enabled()) {
+        char cfg[64];
+        snprintf(cfg, sizeof cfg, "%dx%d waves=%dx%d", BM, BN, WAVES_M, WAVES_N);
+        trace_launch("tiled32", cfg, G, BITS, probs, count, unsigned(total), 64u * WAVES_M * WAVES_N, 0u);
+    }
+    return e;
 }
 
 template <int BITS, int G>

@@ -6,11 +6,31 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
 #include "../../include/lowbit.h"
 #include "lowbit_internal.h"
+
+namespace lowbit {
+
+bool trace_enabled() {
+    const char* v = std::getenv("LOWBIT_TRACE");
+    return v != nullptr && v[0] != 0 && std::strcmp(v, "0") != 0;
+}
+
+void trace_launch(const char* family, const char* config, int g, int bits, const GemmProblem* probs, int count,
+                  unsigned grid, unsigned block, unsigned lds) {
+    char line[1024];
+    int n = snprintf(line, sizeof line, "lowbit: %s %s g=%d bits=%d grid=%u block=%u lds=%u problems=", family, config,
+                     g, bits, grid, block, lds);
+    for (int i = 0; i < count && n > 0 && n < int(sizeof line) - 48; ++i)
+        n += snprintf(line + n, sizeof line - size_t(n), "%s%dx%dx%d", i ? "," : "", probs[i].M, probs[i].N, probs[i].K);
+    std::fprintf(stderr, "%s\n", line);
+}
+
+}  // namespace lowbit
 
 namespace {
 

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdio.h>
 #include <stdint.h>
 
 namespace lowbit {
@@ -33,6 +34,13 @@ struct ProblemGroup {
     int tile_end[kMaxGroup];
     int count;
 };
+
+// LOWBIT_TRACE=1 (read at every launch): one line per GEMM kernel launch on stderr, naming the
+// kernel family and its configuration, g, bits, grid and workgroup size, dynamic LDS, and the
+// problems (M x N x K) of the launch.
+bool trace_enabled();
+void trace_launch(const char* family, const char* config, int g, int bits, const GemmProblem* probs, int count,
+                  unsigned grid, unsigned block, unsigned lds);
 
 hipError_t launch_pack(const int8_t* codes, uint32_t* W, int64_t N, int64_t K, int bits,
                        int32_t* bad_count, hipStream_t stream);

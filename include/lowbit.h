@@ -295,7 +295,14 @@ int lowbit_gemm_affine(const void* X, const uint32_t* W, const void* S, const vo
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,
                            int64_t M, int64_t N, int64_t K, int g, int bits);
 
-/* Name of the kernel variant lowbit_gemm picks for a shape (for logs and tests). */
+/* Name of the kernel variant lowbit_gemm picks for a shape (for logs and tests).
+ *
+ * Launch log: with the environment variable LOWBIT_TRACE set (to anything but "" or "0", read at
+ * every launch), each GEMM kernel launch of every entry point writes one line to stderr:
+ *   lowbit: <family> <configuration> g=<g> bits=<bits> grid=<workgroups> block=<threads>
+ *           lds=<dynamic LDS bytes> problems=<M>x<N>x<K>[,<M>x<N>x<K>...]
+ * (one line; family resident, skinny, tile16 or tiled32; the configuration names the tile and
+ * wave layout, or the resident plan's column blocks, K slices, steps, splits and tiles). */
 const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 /* Human-readable text for a status code. */
