@@ -322,7 +322,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             }
         };
 
-        auto compute = [&](const unsigned char* xt, const Ops& o) __attribute__((always_inline)) {
+        // `issue` runs after the first row block's MFMAs: the next step's copies go out once the
+        // step's first operand reads, expansion and MFMAs are under way, not in a burst with them
+        // right after the barrier (measured 3% faster on the 4608-row denoise shapes).
+        auto compute = [&](const unsigned char* xt, const Ops& o, auto&& issue) __attribute__((always_inline)) {
             // Codes of column block nb are expanded just before its first MFMA pair (row block 0),
             // behind a scheduling fence: the expansion of block nb + 1 then runs while the matrix
             // core works on block nb, instead of every wave of a SIMD expanding all its codes
@@ -362,6 +365,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
             int pb = -1;  // previous block, its partial sum in tmp[pb & 1]
 #pragma unroll
             for (int mb = 0; mb < C::MB; ++mb) {
+                if (mb == (C::MB > 1 ? 1 : 0)) issue();
                 if (mb + 1 < C::MB) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
@@ -460,21 +464,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 #pragma nounroll
         for (; step + 1 < kend; step += 2) {
             read_operands(w_buf(step), s_buf(step), AFFINE ? b_buf(step) : nullptr, step, ops);
-            prefetch_x(step, xa1);
-            prefetch_blocks(step);
-            compute(xa0, ops);
+            compute(xa0, ops, [&]() __attribute__((always_inline)) {
+                prefetch_x(step, xa1);
+                prefetch_blocks(step);
+            });
             wait_vmcnt0();
             __syncthreads();
             read_operands(w_buf(step + 1), s_buf(step + 1), AFFINE ? b_buf(step + 1) : nullptr, step + 1, ops);
-            prefetch_x(step + 1, xa0);
-            prefetch_blocks(step + 1);
-            compute(xa1, ops);
+            compute(xa1, ops, [&]() __attribute__((always_inline)) {
+                prefetch_x(step + 1, xa0);
+                prefetch_blocks(step + 1);
+            });
             wait_vmcnt0();
             __syncthreads();
         }
         if (step < kend) {
             read_operands(w_buf(step), s_buf(step), AFFINE ? b_buf(step) : nullptr, step, ops);
-            compute(xa0, ops);
+            compute(xa0, ops, []() {});
         }
 
         // ---- K groups: group 1's sums through LDS, added to group 0's (order 0, 1) ----

@@ -220,7 +220,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
         }
     };
 
-    auto compute = [&](const unsigned char* xt, const Ops& o, int step) {
+    // `issue` runs once the first row block's MFMAs of the step are under way: the next step's
+    // copies then do not go out in a burst with the step's first operand reads and expansion.
+    auto compute = [&](const unsigned char* xt, const Ops& o, int step, auto&& issue) {
 #pragma unroll
         for (int q = 0; q < C::GPS; ++q) {
             if (C::GPS > 1 && step * C::GPS + q >= ksub) break;  // K tail (g = 32, K % 64 == 32)
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
             bf16x8_t afr[C::CHUNKS];
 #pragma unroll
             for (int b = 0; b <= C::MB * C::NB; ++b) {
+                if (q == 0 && b == (C::MB > 1 && C::GPS == 1 ? C::NB : 0)) issue();
                 if (b < C::MB * C::NB) {
                     const int mb = b / C::NB, nb = b % C::NB;
                     if (nb == 0) {
@@ -303,16 +306,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
     Ops ops;
     for (int step = 0; step < ksteps; step += 2) {
         read_operands(w_buf(step), s_buf(step), step, ops);
-        prefetch_x(step, xa1);
-        prefetch_blocks(step);
-        compute(xa0, ops, step);
+        compute(xa0, ops, step, [&]() {
+            prefetch_x(step, xa1);
+            prefetch_blocks(step);
+        });
         wait_vmcnt0();
         __syncthreads();
         if (step + 1 >= ksteps) break;
         read_operands(w_buf(step + 1), s_buf(step + 1), step + 1, ops);
-        prefetch_x(step + 1, xa0);
-        prefetch_blocks(step + 1);
-        compute(xa1, ops, step + 1);
+        compute(xa1, ops, step + 1, [&]() {
+            prefetch_x(step + 1, xa0);
+            prefetch_blocks(step + 1);
+        });
         wait_vmcnt0();
         __syncthreads();
     }
