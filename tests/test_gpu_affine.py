@@ -107,10 +107,14 @@ def test_one_hot_level_is_exact():
         assert not np.any(np.delete(y, n0, axis=1) & 0x7FFF)
 
 
-def test_one_hot_bias_is_exact():
+@pytest.mark.parametrize("variant", [None, "tile288", "tile96", "tile96k2", "tile64k2"])
+def test_one_hot_bias_is_exact(variant, monkeypatch):
     """Zero scales, one nonzero bias b at (n0, group j) and one nonzero activation per row at k0
     in group j: Y[:, n0] = RNE_bf16(b * x[:, k0]) exactly (the bias path's activation sum of a
-    single element), every other column 0."""
+    single element), every other column 0; on every tile (fp32 FMAs per group on the 12-wave
+    tile, a bias MFMA per four groups on the others)."""
+    if variant is not None:
+        monkeypatch.setenv("LOWBIT_VARIANT", variant)
     M, N, K, g = 24, 48, 384, 128
     inp = W.make_inputs(_problem(M, N, K, g, cid=124), seed=5)
     s = np.zeros_like(inp.scales)
@@ -123,6 +127,19 @@ def test_one_hot_bias_is_exact():
         want = oracle.f64_to_bf16_bits_rne(float(b[n0, k0 // g]) * oracle.bf16_bits_to_f64(x[:, k0]))
         assert np.array_equal(y[:, n0], want), (n0, k0)
         assert not np.any(np.delete(y, n0, axis=1) & 0x7FFF)
+
+
+@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2", "tile64k2"])
+@pytest.mark.parametrize("K,g", [(384, 64), (384, 128), (1408, 64), (1408, 128), (64, 64)])
+def test_bias_sets_across_k_groups(variant, K, g, monkeypatch):
+    """The bias terms of sets of four groups: K ranges that start or end inside a set (K split
+    between two groups of waves at 3 or 11 steps each, g = 128 splitting a group between them),
+    several full sets, a single step, ragged M and N."""
+    monkeypatch.setenv("LOWBIT_VARIANT", variant)
+    M, N = 100, 208
+    inp = W.make_inputs(_problem(M, N, K, g, cid=128), seed=8)
+    y, _ = _run(inp, g)
+    _check(y, inp, g, f"bias sets {variant} K={K} g{g}")
 
 
 def test_shifted_symmetric_weights_match_the_int4_path():

@@ -105,3 +105,23 @@ def test_fused_epilogues_multi_round():
     got = host_bits(Rd)
     r = oracle.check_tolerance(got[rows], oracle.residual_ref_f64(inp.x[rows], inp.codes, inp.scales, 64, R[rows], gate))
     assert r["ok"], r
+
+
+@pytest.mark.parametrize("M,N,K,g", [(288, 192 * 257, 128, 64),          # 257 tiles: one workgroup runs two
+                                     (7 * 288, 73 * 192, 128, 64),       # 511 tiles: one workgroup runs one
+                                     (16 * 288, 32 * 192, 64, 64),       # 512 tiles, a single K step each
+                                     (27 * 288 - 5, 19 * 192 - 16, 128, 128)])  # 513 tiles, ragged edges
+def test_tile_counts_around_whole_rounds(M, N, K, g, monkeypatch):
+    """Tile counts one below, at and one above a multiple of the 256 workgroups: the loop's exit
+    (next virtual id past the tile count) on every workgroup, and the last round's odd tile."""
+    monkeypatch.setenv("LOWBIT_VARIANT", "tile288")
+    print(f"persistent edges {M}x{N}x{K} g={g} tiles={_tiles(M, N)}", flush=True)
+    inp, x, w, s = _inputs(M, N, K, g, 2, cid=146)
+    y = host_bits(lb.gemm(x, w, s, g, 2))
+    rows = _rows(M)
+    r = oracle.check_tolerance(y[rows], oracle.gemm_ref_f64(inp.x[rows], inp.codes, inp.scales, g))
+    assert r["ok"], r
+    # the last tile (highest virtual id) in full
+    r0, c0 = ((M - 1) // 288) * 288, ((N - 1) // 192) * 192
+    ref = oracle.gemm_ref_f64(inp.x[r0:], inp.codes[c0:], inp.scales[c0:], g)
+    assert oracle.check_tolerance(y[r0:, c0:], ref)["ok"]
