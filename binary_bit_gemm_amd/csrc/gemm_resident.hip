@@ -25,6 +25,7 @@
 // word, all inside one 64-code piece, and the piece's group scale multiplies the MFMA's
 // partial sum in fp32 (w = scale_g * b, model card "Binary Weight Representation: 1-bit
 // g128").  The operand holds 2c; the factor 1/2 is applied once to the final sum.
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 
@@ -362,11 +363,19 @@ __global__ __launch_bounds__(64 * kMaxWaves, 1) void gemm_resident_kernel(Reside
 
 template <int G, int LEN, int EPI = kEpiPlain>
 hipError_t launch_cfg(const ResidentArgs& a, uint32_t lds, hipStream_t stream) {
-    // allow the dynamic LDS of the largest plan (once per kernel)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN, EPI>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        kMaxLds);
-    if (attr != hipSuccess) return attr;
+    // allow the dynamic LDS of the largest plan, once per kernel and device (threads that get here
+    // first at the same time may both set it; the value is the same)
+    static std::atomic<int> attr_set[64];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (attr_set[dev].load(std::memory_order_acquire) == 0) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_resident_kernel<G, LEN, EPI>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (err != hipSuccess) return err;
+        attr_set[dev].store(1, std::memory_order_release);
+    }
     hipLaunchKernelGGL((gemm_resident_kernel<G, LEN, EPI>), dim3(a.tiles * a.splits), dim3(64 * a.cb * a.ks), lds,
                        stream, a);
     const hipError_t e = hipGetLastError();
