@@ -27,6 +27,7 @@ int forced_tile() {
     if (std::strcmp(v, "tile288") == 0) return TILE_288x192;
     if (std::strcmp(v, "tile96") == 0) return TILE_96x192;
     if (std::strcmp(v, "tile96k2") == 0) return TILE_96x192K2;
+    if (std::strcmp(v, "tile256n") == 0) return TILE_256x192;
     if (std::strcmp(v, "tile64k2") == 0) return TILE_64x128K2;
     return -1;
 }

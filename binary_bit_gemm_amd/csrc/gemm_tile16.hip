@@ -654,6 +654,7 @@ hipError_t launch_variant16(const GemmProblem* probs, int count, int variant, hi
         return launch_cfg16<G, BITS, 96, 192, 1, 4, 1, kEpiPlain, AFFINE>(probs, count, stream);
     }
     if (variant == TILE_96x192) return launch_cfg16<G, BITS, 96, 192, 1, 4, 1, kEpiPlain, AFFINE>(probs, count, stream);
+    if (variant == TILE_256x192) return launch_cfg16<G, BITS, 256, 192, 2, 6, 1, kEpiPlain, AFFINE>(probs, count, stream);
     return launch_cfg16<G, BITS, 288, 192, 2, 6, 1, kEpiPlain, AFFINE>(probs, count, stream);
 }
 

@@ -391,6 +391,7 @@ struct TileShape {
 constexpr TileShape kTiles[] = {
     {TILE_256x256, 256, 256, 1, 1.00f, 1.00f},
     {TILE_288x192, 288, 192, 1, 0.87f, 0.82f},
+    {TILE_256x192, 256, 192, 1, 0.87f, 0.82f},
     {TILE_128x256, 128, 256, 2, 0.92f, 0.92f},
     {TILE_64x256, 64, 256, 2, 0.75f, 0.75f},
     {TILE_96x192, 96, 192, 1, 0.54f, 0.51f},
@@ -450,6 +451,7 @@ const char* tile_variant_name(int variant) {
         case TILE_96x192: return "tile96x192";
         case TILE_96x192K2: return "tile96x192k2";
         case TILE_64x128K2: return "tile64x128k2";
+        case TILE_256x192: return "tile256x192";
         default: return "tile64x256";
     }
 }

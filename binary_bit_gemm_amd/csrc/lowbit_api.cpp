@@ -77,8 +77,8 @@ int device_check() {
 }
 
 // Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | resident | tile256 | tile256w |
-// tile128 | tile64 | tile288 | tile96 | tile96k2 (the last three fall back to tile256w where the 16x16
-// kernel does not apply)
+// tile128 | tile64 | tile288 | tile256n (256 x 192) | tile96 | tile96k2 | tile64k2 (the 16x16-block tiles,
+// tile288 onwards, fall back to tile256w where that kernel does not apply)
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
@@ -90,6 +90,7 @@ int forced_variant() {
     if (std::strcmp(v, "tile288") == 0) return lowbit::TILE_288x192;
     if (std::strcmp(v, "tile96") == 0) return lowbit::TILE_96x192;
     if (std::strcmp(v, "tile96k2") == 0) return lowbit::TILE_96x192K2;
+    if (std::strcmp(v, "tile256n") == 0) return lowbit::TILE_256x192;
     if (std::strcmp(v, "tile64k2") == 0) return lowbit::TILE_64x128K2;
     if (std::strcmp(v, "resident") == 0) return 102;
     return -1;

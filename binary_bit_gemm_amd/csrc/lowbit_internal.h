@@ -61,10 +61,11 @@ hipError_t launch_import_binary_gemlite(const uint8_t* src, uint32_t* W, int64_t
 enum TileVariant {
     TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5,
     TILE_96x192K2 = 6,  // 96 x 192 with K split between two groups of 4 waves (even step counts)
-    TILE_64x128K2 = 7   // 64 x 128, the same K split (4-bit codes: small output grids)
+    TILE_64x128K2 = 7,  // 64 x 128, the same K split (4-bit codes: small output grids)
+    TILE_256x192 = 8    // 256 x 192 in 12 waves of 128 x 32 (M = 4096 in whole rounds at N = 3072)
 };
 inline bool is_tile16_variant(int v) {
-    return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2 || v == TILE_64x128K2;
+    return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2 || v == TILE_64x128K2 || v == TILE_256x192;
 }
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
 

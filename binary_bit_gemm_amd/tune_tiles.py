@@ -33,11 +33,13 @@ if ROOT not in sys.path:
 
 # name for LOWBIT_VARIANT -> (tile rows, tile columns, workgroups resident per compute unit)
 TILES = {
-    "tile256w": (256, 256, 1), "tile288": (288, 192, 1), "tile128": (128, 256, 2), "tile64": (64, 256, 2),
+    "tile256w": (256, 256, 1), "tile288": (288, 192, 1), "tile256n": (256, 192, 1), "tile128": (128, 256, 2),
+    "tile64": (64, 256, 2),
     "tile96": (96, 192, 1), "tile96k2": (96, 192, 1), "tile64k2": (64, 128, 1),
 }
 DEFAULT_SHAPES = [(4608, 3072, 3072), (4608, 9216, 3072), (4608, 18432, 3072), (4608, 3072, 9216),
-                  (4608, 3072, 12288), (4096, 4096, 3072), (1536, 3072, 3072), (1536, 9216, 3072)]
+                  (4608, 3072, 12288), (4096, 4096, 3072), (4096, 3072, 3072), (4096, 9216, 3072),
+                  (1536, 3072, 3072), (1536, 9216, 3072)]
 CUS = 256
 
 
@@ -87,7 +89,7 @@ def main() -> None:
     ap.add_argument("--g", type=int, default=64)
     ap.add_argument("--reps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--tiles", default="tile256w,tile288,tile128,tile64,tile96,tile96k2")
+    ap.add_argument("--tiles", default="tile256w,tile288,tile256n,tile128,tile64,tile96,tile96k2")
     ap.add_argument("--shapes", nargs="*", default=None, help="M,N,K triples")
     a = ap.parse_args()
     import binary_bit_gemm_amd as lb

@@ -155,7 +155,7 @@ def test_int4_arguments_and_kernel():
     assert L.lowbit_check_gemm_args(A, A, A, A, 512, 2560, 9728, 64, 3) == UNSUPPORTED
     assert L.lowbit_pack(A, A, 16, 12, 4, None, None) == INVALID          # K % 8
     assert L.lowbit_pack(A, A, 16, 24, 3, None, None) == UNSUPPORTED
-    tile16 = {"tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"}
+    tile16 = {"tile288x192", "tile256x192", "tile96x192", "tile96x192k2", "tile64x128k2"}
     for M, N, K in ((1, 16, 64), (16, 3072, 2560), (512, 19456, 2560), (512, 2560, 9728), (4608, 3072, 3072)):
         assert lb.variant(M, N, K, 64, 4) in tile16, (M, N, K)
 
@@ -163,7 +163,8 @@ def test_int4_arguments_and_kernel():
 def test_int4_forced_variants_stay_on_the_tile16_kernel(monkeypatch):
     for v in ("skinny", "resident", "tile64", "tile256w"):
         monkeypatch.setenv("LOWBIT_VARIANT", v)
-        assert lb.variant(16, 3072, 2560, 64, 4) in {"tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"}, v
+        assert lb.variant(16, 3072, 2560, 64, 4) in {"tile288x192", "tile256x192", "tile96x192", "tile96x192k2",
+                                                     "tile64x128k2"}, v
 
 
 def test_variant_choice():
@@ -184,6 +185,14 @@ def test_variant_choice():
     assert lb.variant(1536, 3072, 9216, 64, 1) == "tile96x192k2"
     assert lb.variant(1536, 3072, 3136, 64, 2) == "tile96x192"  # 49 steps
     assert lb.variant(1536, 9216, 3072, 64, 2) == "tile256x256"
+    # M = 4096 (the image stream's linears as single calls): 256 x 192 tiles make whole rounds at
+    # N = 3072 and 9216 where 288 x 192 needs a 22%-full last row of tiles; at N = 18432 256 x 256
+    # still wins; M = 4608 stays on 288 x 192 (256 x 192 would need 18 rows: 1.125 rounds)
+    assert lb.variant(4096, 3072, 3072, 64, 2) == "tile256x192"
+    assert lb.variant(4096, 9216, 3072, 64, 2) == "tile256x192"
+    assert lb.variant(4096, 3072, 9216, 128, 1) == "tile256x192"
+    assert lb.variant(4096, 18432, 3072, 64, 2) == "tile256x256"
+    assert lb.variant(512, 19456, 2560, 64, 4) == "tile256x192"
     assert not lb.variant(1536, 3072, 3072, 32, 2).startswith("tile96")  # g = 32: 32x32-block kernel only
     assert lb.variant(64, 256, 256, 64, 2).startswith("tile")
 

@@ -79,7 +79,7 @@ def test_affine_matches_oracle(M, N, K, g):
     _check(y, inp, g, f"affine {M}x{N}x{K} g{g}")
 
 
-@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2", "tile64k2"])
+@pytest.mark.parametrize("variant", ["tile288", "tile256n", "tile96", "tile96k2", "tile64k2"])
 @pytest.mark.parametrize("g", [64, 128])
 def test_every_tile_variant(variant, g, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
@@ -107,7 +107,7 @@ def test_one_hot_level_is_exact():
         assert not np.any(np.delete(y, n0, axis=1) & 0x7FFF)
 
 
-@pytest.mark.parametrize("variant", [None, "tile288", "tile96", "tile96k2", "tile64k2"])
+@pytest.mark.parametrize("variant", [None, "tile288", "tile256n", "tile96", "tile96k2", "tile64k2"])
 def test_one_hot_bias_is_exact(variant, monkeypatch):
     """Zero scales, one nonzero bias b at (n0, group j) and one nonzero activation per row at k0
     in group j: Y[:, n0] = RNE_bf16(b * x[:, k0]) exactly (the bias path's activation sum of a
@@ -129,7 +129,7 @@ def test_one_hot_bias_is_exact(variant, monkeypatch):
         assert not np.any(np.delete(y, n0, axis=1) & 0x7FFF)
 
 
-@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2", "tile64k2"])
+@pytest.mark.parametrize("variant", ["tile288", "tile256n", "tile96", "tile96k2", "tile64k2"])
 @pytest.mark.parametrize("K,g", [(384, 64), (384, 128), (1408, 64), (1408, 128), (64, 64)])
 def test_bias_sets_across_k_groups(variant, K, g, monkeypatch):
     """The bias terms of sets of four groups: K ranges that start or end inside a set (K split

@@ -102,7 +102,8 @@ def test_gemm_small(M, N, K, g, bits):
     _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{M}x{N}x{K} g{g} b{bits}")
 
 
-@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "tile288", "tile96", "tile96k2", "skinny"])
+@pytest.mark.parametrize("variant", ["tile256", "tile256w", "tile128", "tile64", "tile288", "tile256n", "tile96", "tile96k2",
+                                     "skinny"])
 @pytest.mark.parametrize("M", [16, 300, 600])
 def test_every_variant(variant, M, monkeypatch):
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
@@ -113,17 +114,17 @@ def test_every_variant(variant, M, monkeypatch):
             _assert_parity(y, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, g), f"{variant} M={M} g{g} b{bits}")
 
 
-@pytest.mark.parametrize("variant", ["tile288", "tile96", "tile96k2"])
+@pytest.mark.parametrize("variant", ["tile288", "tile256n", "tile96", "tile96k2"])
 @pytest.mark.parametrize("bits", [2, 1])
 @pytest.mark.parametrize("M,N,K,g", [(600, 400, 1280, 64), (300, 592, 3072, 128), (289, 208, 64, 64),
                                      (577, 192, 8448, 128)])
 def test_tile16_several_blocks(M, N, K, g, bits, variant, monkeypatch):
-    # the 16x16-block kernel (288 x 192 and 96 x 192 tiles) over several weight blocks (64
+    # the 16x16-block kernel (288 x 192, 256 x 192 and 96 x 192 tiles) over several weight blocks (64
     # bytes of a row: 4 ternary or 8 binary steps) and scale blocks, a last weight block that
     # runs past the row (K % 512 != 0 for binary), a single step, and ragged tiles in both
     # directions
     monkeypatch.setenv("LOWBIT_VARIANT", variant)
-    assert lb.variant(M, N, K, g, bits) == {"tile288": "tile288x192", "tile96": "tile96x192",
+    assert lb.variant(M, N, K, g, bits) == {"tile288": "tile288x192", "tile256n": "tile256x192", "tile96": "tile96x192",
                                             "tile96k2": "tile96x192k2"}[variant]
     inp = _inputs(M, N, K, g, bits, seed=11)
     y, _ = run_gemm(inp, g, bits)

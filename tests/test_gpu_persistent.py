@@ -125,3 +125,21 @@ def test_tile_counts_around_whole_rounds(M, N, K, g, monkeypatch):
     r0, c0 = ((M - 1) // 288) * 288, ((N - 1) // 192) * 192
     ref = oracle.gemm_ref_f64(inp.x[r0:], inp.codes[c0:], inp.scales[c0:], g)
     assert oracle.check_tolerance(y[r0:, c0:], ref)["ok"]
+
+
+@pytest.mark.parametrize("g,bits", [(64, 2), (128, 1)])
+def test_256x192_multi_round_ragged(g, bits, monkeypatch):
+    """The 256 x 192 tile (12 waves of 128 x 32) persistent over three rounds, with a ragged last
+    row and column of tiles."""
+    M, N, K = 4096 - 7, 9216 - 16, 384
+    assert math.ceil(M / 256) * math.ceil(N / 192) == 768
+    monkeypatch.setenv("LOWBIT_VARIANT", "tile256n")
+    assert lb.variant(M, N, K, g, bits) == "tile256x192"
+    print(f"persistent 256x192 {M}x{N}x{K} g={g} bits={bits}", flush=True)
+    inp, x, w, s = _inputs(M, N, K, g, bits, cid=147)
+    y = host_bits(lb.gemm(x, w, s, g, bits))
+    rows = np.array(sorted({0, 1, 255, 256, 257, 2047, 2048, M - 250, M - 1}))
+    r = oracle.check_tolerance(y[rows], oracle.gemm_ref_f64(inp.x[rows], inp.codes, inp.scales, g))
+    assert r["ok"], r
+    cols = slice(N - 200, N)  # the ragged last column of tiles and its neighbour
+    assert oracle.check_tolerance(y[:, cols], oracle.gemm_ref_f64(inp.x, inp.codes[cols], inp.scales[cols], g))["ok"]

@@ -34,7 +34,7 @@ def _family(variant: str) -> tuple[str, str]:
     m = re.match(r"tile(\d+)x(\d+)(k2)?$", variant)
     assert m, variant
     tile = f"{m.group(1)}x{m.group(2)}"
-    if variant in ("tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"):
+    if variant in ("tile288x192", "tile256x192", "tile96x192", "tile96x192k2", "tile64x128k2"):
         return "tile16", tile
     return "tiled32", tile
 

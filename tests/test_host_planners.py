@@ -14,7 +14,7 @@ import binary_bit_gemm_amd as lb
 OK, INVALID, UNSUPPORTED, ALIGN = 0, 1, 2, 3
 COUNTER_BYTES = 4096
 KNOWN = {"skinny", "resident", "tile256x128", "tile256x256", "tile128x256", "tile64x256", "tile288x192",
-         "tile96x192", "tile96x192k2", "tile64x128k2"}
+         "tile256x192", "tile96x192", "tile96x192k2", "tile64x128k2"}
 
 MS = [0, 1, 2, 7, 15, 16, 17, 31, 32, 33, 64, 300, 512, 1024, 1535, 1536, 4096, 4608, 9000]
 NS = [0, 16, 48, 256, 272, 1040, 3072, 9216, 18432, 27648, 36864]
@@ -37,7 +37,7 @@ def test_variant_and_workspace_sweep():
         v = lb.variant(M, N, K, g, bits)
         assert v in KNOWN, (M, N, K, g, bits, v)
         if bits == 4:
-            assert v in ("tile288x192", "tile96x192", "tile96x192k2", "tile64x128k2"), v
+            assert v in ("tile288x192", "tile256x192", "tile96x192", "tile96x192k2", "tile64x128k2"), v
         ws = lb.workspace_size(M, N, K, g, bits)
         if ws:
             # only skinny ternary shapes split K, and every automatic plan fits the static scratch
