@@ -196,3 +196,34 @@ def test_workspace_shared_by_launches_of_different_tile_counts():
     for inp, (x, w, s, y, g, bits) in items:
         _check(host_bits(y), inp, g, f"batched, shared workspace {tuple(x.shape)}x{w.shape[0]}")
     assert not ws[:COUNTER_BYTES].any().item(), "arrival counters not reset"
+
+
+def test_concurrent_streams_with_their_own_workspaces():
+    """Two streams, each with its own workspace, run split-K calls at the same time: every result
+    is bitwise its single-stream result and both counter regions end at zero."""
+    t = torch()
+    M, g = 16, 64
+    data = []
+    for i, (N, K) in enumerate(((3072, 12288), (3072, 9216))):
+        inp = _inputs(M, N, K, g, seed=20 + i, cid=90 + i)
+        x, w, s = _dev(inp)
+        ws = _workspace(lb.workspace_size(M, N, K, g, 2))
+        ref = host_bits(lb.gemm(x, w, s, g, 2, workspace=ws))
+        _check(ref, inp, g, f"split N={N} K={K}")
+        data.append((x, w, s, ws, ref, t.empty((M, N), dtype=t.bfloat16, device="cuda")))
+    streams = [t.cuda.Stream(), t.cuda.Stream()]  # default priority
+    for st in streams:
+        st.wait_stream(t.cuda.current_stream())
+    outs = [[], []]
+    for _ in range(20):
+        for (x, w, s, ws, _ref, y), st, o in zip(data, streams, outs):
+            with t.cuda.stream(st):
+                lb.gemm(x, w, s, g, 2, out=y, workspace=ws)
+                o.append(y.clone())
+    for st in streams:
+        t.cuda.current_stream().wait_stream(st)
+    t.cuda.synchronize()
+    for (_x, _w, _s, ws, ref, _y), o in zip(data, outs):
+        for y in o:
+            assert np.array_equal(host_bits(y), ref)
+        assert not ws[:COUNTER_BYTES].any().item(), "arrival counters not reset"
