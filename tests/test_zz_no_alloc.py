@@ -73,3 +73,38 @@ def test_noalloc_rejects_a_plan_larger_than_its_scratch(monkeypatch):
     assert e.value.status == 6
     torch().cuda.synchronize()
     assert torch().isnan(y.float()).all().item(), "nothing may be written"
+
+
+def test_noalloc_under_graph_capture():
+    """The caller this entry point is for: a captured call replayed several times, with eager work
+    and an eager call of another shape on the same scratch between replays, gives the eager result
+    every time (the counter clear is a fill kernel, not a memset, and every partial sum is written
+    before it is read)."""
+    t = torch()
+    inp, x, w, s, y = _case(16, 3072, 12288, 64, cid=96)
+    o_inp, ox, ow, os_, oy = _case(8, 1024, 6144, 64, cid=97)
+    print("noalloc graph 16x3072x12288 g=64", flush=True)
+    lb.gemm_noalloc(x, w, s, 64, 2, out=y)
+    t.cuda.synchronize()
+    eager = host_bits(y)
+    r = oracle.check_tolerance(eager, oracle.gemm_ref_f64(inp.x, inp.codes, inp.scales, 64))
+    assert r["ok"], r
+    st = t.cuda.Stream()  # default priority
+    st.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(st):
+        lb.gemm_noalloc(x, w, s, 64, 2, out=y)  # warm up on the capture stream
+    t.cuda.current_stream().wait_stream(st)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        lb.gemm_noalloc(x, w, s, 64, 2, out=y)
+    other = None
+    for rep in range(4):
+        y.fill_(float("nan"))
+        lb.gemm_noalloc(ox, ow, os_, 64, 2, out=oy)  # another split on the same scratch
+        t.cuda.synchronize()
+        other = host_bits(oy) if other is None else other
+        assert np.array_equal(host_bits(oy), other)
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(host_bits(y), eager), f"replay {rep}"
