@@ -27,8 +27,8 @@ def _device():
     yield
 
 
-def _tiles(M, N):
-    return math.ceil(M / 288) * math.ceil(N / 192)
+def _tiles(M, N, bm=288):
+    return math.ceil(M / bm) * math.ceil(N / 192)
 
 
 def _inputs(M, N, K, g, bits, cid):
@@ -60,11 +60,12 @@ def test_multi_round_ragged(M, N, K, g, bits, monkeypatch):
     assert np.array_equal(host_bits(lb.gemm(x, w, s, g, bits)), y), "not deterministic"
 
 
-def test_grouped_tiles_span_problems(monkeypatch):
-    monkeypatch.setenv("LOWBIT_VARIANT", "tile288")
+@pytest.mark.parametrize("variant,bm", [("tile288", 288), ("tile256n", 256)])
+def test_grouped_tiles_span_problems(variant, bm, monkeypatch):
+    monkeypatch.setenv("LOWBIT_VARIANT", variant)
     t = torch()
     shapes = [(1200, 4096, 512), (700, 6144, 1024), (2000, 2048, 256)]
-    assert sum(_tiles(M, N) for M, N, _ in shapes) > 256
+    assert sum(_tiles(M, N, bm) for M, N, _ in shapes) > 256
     items = []
     for i, (M, N, K) in enumerate(shapes):
         inp, x, w, s = _inputs(M, N, K, 64, 2, cid=141 + i)
