@@ -66,6 +66,48 @@ def kernel_source_sha(variants, read=None) -> str:
     return h.hexdigest()
 
 
+def variant_of_trace_line(line: str):
+    """The kernel variant name of one LOWBIT_TRACE line ("lowbit: <family> <tile or plan> ..."),
+    or None for other lines.  The 16x16-block tiles name their K split as waves=MxNxK."""
+    import re
+    m = re.match(r"lowbit: (\w+) (\S+)(?: waves=(\d+)x(\d+)(?:x(\d+))?)?", line)
+    if not m:
+        return None
+    family, tile, ksplit = m.group(1), m.group(2), m.group(5)
+    if family in ("resident", "skinny"):
+        return family
+    if family == "tile16" and (ksplit == "2" or tile == "64x128"):
+        return f"tile{tile}k2"  # 64 x 128 runs under that variant name with or without the split
+    return f"tile{tile}"
+
+
+def launched_variants(run_step):
+    """The GEMM kernel variants one step launches, read from the library's launch log
+    (LOWBIT_TRACE) with stderr sent to a temporary file around that one step; grouped calls can
+    launch another tile than their problems' single calls would."""
+    import tempfile
+    import torch
+    torch.cuda.synchronize()
+    sys.stderr.flush()
+    saved_fd, saved_env = os.dup(2), os.environ.get("LOWBIT_TRACE")
+    with tempfile.TemporaryFile() as log:
+        os.dup2(log.fileno(), 2)
+        os.environ["LOWBIT_TRACE"] = "1"
+        try:
+            run_step()
+            torch.cuda.synchronize()
+        finally:
+            if saved_env is None:
+                os.environ.pop("LOWBIT_TRACE", None)
+            else:
+                os.environ["LOWBIT_TRACE"] = saved_env
+            os.dup2(saved_fd, 2)
+            os.close(saved_fd)
+        log.seek(0)
+        lines = log.read().decode(errors="replace").splitlines()
+    return sorted({v for v in (variant_of_trace_line(l) for l in lines) if v is not None})
+
+
 def measured_traffic(workload: str, variants):
     """HBM bytes per launch of the workload's kernels from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy), or
@@ -329,6 +371,7 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    variants = launched_variants(step)  # one more warm-up step, with the launch log on
 
     # optionally the step as one HIP graph (captured on a side stream, replayed on the current one)
     graph = None
@@ -383,7 +426,6 @@ def main():
     launch_ms = event_ms / launches
     kern_tflops = flops_step / (event_ms * 1e-3) / 1e12
     kern_gbs = bytes_step / (event_ms * 1e-3) / 1e9
-    variants = sorted({lb.variant(p.M, p.N, p.K, p.g, p.bits) for p in probs})
     traffic = measured_traffic(a.workload, variants)
 
     if a.workload in ("skinny", "swiglu16"):
