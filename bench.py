@@ -37,6 +37,7 @@ VARIANT_SOURCES = {
     "tile256x256": ["gemm_tiled.hip"], "tile256x128": ["gemm_tiled.hip"], "tile128x256": ["gemm_tiled.hip"],
     "tile64x256": ["gemm_tiled.hip"], "tile288x192": ["gemm_tile16.hip"], "tile96x192": ["gemm_tile16.hip"],
     "tile96x192k2": ["gemm_tile16.hip"], "tile64x128k2": ["gemm_tile16.hip"], "tile256x192": ["gemm_tile16.hip"],
+    "tile256x256sk": ["gemm_tiled.hip"],
     "skinny": ["gemm_skinny.hip"],
     "resident": ["gemm_resident.hip"],
 }
@@ -68,7 +69,8 @@ def kernel_source_sha(variants, read=None) -> str:
 
 def variant_of_trace_line(line: str):
     """The kernel variant name of one LOWBIT_TRACE line ("lowbit: <family> <tile or plan> ..."),
-    or None for other lines.  The 16x16-block tiles name their K split as waves=MxNxK."""
+    or None for other lines.  The 16x16-block tiles name their K split as waves=MxNxK; a stream-K
+    launch of the 256 x 256 tile says "streamk" after its waves."""
     import re
     m = re.match(r"lowbit: (\w+) (\S+)(?: waves=(\d+)x(\d+)(?:x(\d+))?)?", line)
     if not m:
@@ -78,6 +80,8 @@ def variant_of_trace_line(line: str):
         return family
     if family == "tile16" and (ksplit == "2" or tile == "64x128"):
         return f"tile{tile}k2"  # 64 x 128 runs under that variant name with or without the split
+    if family == "tiled32" and " streamk" in line:
+        return f"tile{tile}sk"
     return f"tile{tile}"
 
 

@@ -29,6 +29,7 @@ int forced_tile() {
     if (std::strcmp(v, "tile96k2") == 0) return TILE_96x192K2;
     if (std::strcmp(v, "tile256n") == 0) return TILE_256x192;
     if (std::strcmp(v, "tile64k2") == 0) return TILE_64x128K2;
+    if (std::strcmp(v, "tile256sk") == 0) return TILE_256x256SK;
     return -1;
 }
 
@@ -118,6 +119,21 @@ hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int b
         }
         if (nt > 0) {
             const int variant = forced >= 0 ? forced : pick_tile_variant(tiled, nt, g, bits);
+            if (variant == TILE_256x256SK) {
+                // one stream-K launch per problem where the workspace holds its partial tiles
+                int rest = 0;
+                for (int i = 0; i < nt; ++i) {
+                    const size_t need = streamk_workspace_bytes(tiled[i], g, bits);
+                    if (need > 0 && workspace != nullptr && need <= workspace_bytes) {
+                        const hipError_t e = launch_gemm_streamk(tiled[i], g, bits, workspace, workspace_bytes, stream);
+                        if (e != hipSuccess) return e;
+                    } else {
+                        tiled[rest++] = tiled[i];
+                    }
+                }
+                nt = rest;
+                if (nt == 0) continue;
+            }
             const hipError_t e = launch_gemm_tiled_group(tiled, nt, g, bits, variant, stream);
             if (e != hipSuccess) return e;
         }
@@ -126,6 +142,14 @@ hipError_t launch_gemm_grouped(const GemmProblem* probs, int count, int g, int b
 }
 
 size_t grouped_workspace_bytes(const GemmProblem* probs, int count, int g, int bits) {
+    if (forced_tile() == TILE_256x256SK) {
+        size_t need = 0;
+        for (int i = 0; i < count; ++i) {
+            const size_t b = streamk_workspace_bytes(probs[i], g, bits);
+            need = b > need ? b : need;
+        }
+        return need;
+    }
     if (forced_tile() >= 0) return 0;
     const int kind = forced_skinny_kind();
     size_t need = 0;

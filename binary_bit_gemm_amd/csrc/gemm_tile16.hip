@@ -603,7 +603,7 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
     constexpr int kOutBn = EPI == kEpiSwiglu ? BN / 2 : BN;
     for (int i = 0; i < count; ++i) {
         grp.p[i] = probs[i];
-        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + kOutBn - 1) / kOutBn);
+        total += int(tiles_of(probs[i].M, BM) * tiles_of(probs[i].N, kOutBn));
         grp.tile_end[i] = total;
     }
     grp.count = count;

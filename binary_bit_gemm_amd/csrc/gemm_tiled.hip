@@ -38,6 +38,13 @@ constexpr int kChunksPerRow = KS / 8;     // 16-byte chunks per X row
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// 16-byte direct-to-LDS copy with the sc1 cache policy (device-coherent: data other workgroups
+// stored the same way); lane i's 16 bytes land at lds_wave_base + 16 * i.
+__device__ __forceinline__ void dma16_sc1(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0,
+                                            0, 16);
+}
+
 __device__ __forceinline__ int x_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4); }
 
 // Packed-weight block: WB (32 or 64) bytes per row = WB/16 chunks of 16 bytes; chunk c of row
@@ -70,8 +77,20 @@ struct Cfg {
     static_assert(W_LOADS % 64 == 0 && S_LOADS % 64 == 0, "blocks are whole waves of copies");
 };
 
-template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(ProblemGroup grp) {
+// Stream-K launch (SK = true, one problem): a grid of `nwg` workgroups, workgroup w owning the
+// (tile, step) units [w U / nwg, (w + 1) U / nwg) of the U = tiles x steps units in tile-major
+// order.  A tile whose steps span several workgroups is finished by one of them from fp32
+// partial tiles in the workspace: `counters` (zero between calls, one per split tile, indexed
+// by the workgroup that owns the tile's last step) and `parts` (two partial-tile slots per
+// workgroup: the tile of its first unit, the tile of its last).
+struct StreamK {
+    uint32_t* counters;
+    unsigned char* parts;
+    int nwg;
+};
+
+template <int BITS, int G, int BM, int BN, int WAVES_M, int WAVES_N, int WB, bool SK = false>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(ProblemGroup grp, StreamK sk) {
     using C = Cfg<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>;
     // Separate static buffers (not one array indexed by parity): the compiler can then see
     // that reads of one buffer do not depend on copies still landing in the other.
@@ -82,22 +101,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
     __shared__ __attribute__((aligned(16))) unsigned char sk0[C::S_BLOCK];
     __shared__ __attribute__((aligned(16))) unsigned char sk1[C::S_BLOCK];
 
-    // Workgroup -> (problem, tile); the tiles one XCD runs are contiguous in the group's
-    // tile order.
-    const int t = xcd_remap(blockIdx.x, grp.tile_end[grp.count - 1]);
-    int pi = 0;
-    while (pi + 1 < grp.count && t >= grp.tile_end[pi]) ++pi;
-    const GemmProblem p = grp.p[pi];
-    const int tile = t - (pi > 0 ? grp.tile_end[pi - 1] : 0);
-    const int M = p.M, N = p.N, K = p.K;
-    const int tiles_n = (N + BN - 1) / BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
     const int half = lane >> 5, col = lane & 31;
+    f32x16_t acc[C::MB][C::NB];
 
+    // Steps [kb, ke) of tile `tile` of problem p, summed into acc from zero.
+    auto run = [&](const GemmProblem& p, int tile, int kb, int ke) __attribute__((always_inline)) {
+    const int M = p.M, N = p.N, K = p.K;
+    const int tiles_n = (N + BN - 1) / BN;
     const int tm = tile / tiles_n, tn = tile % tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
@@ -172,7 +187,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
         s_rd[nb] = r * 32 + int((uint32_t(n) * s_row_bytes) & 15u);
     }
 
-    f32x16_t acc[C::MB][C::NB];
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -285,26 +299,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
     const int w_blocks = (ksteps + C::W_SPB - 1) / C::W_SPB;
     const int s_blocks = (kgroups + C::S_GPB - 1) / C::S_GPB;
 
-    // During step s: X of step s+1, and -- on the first step of a weight or scale block --
-    // the whole next block into the other buffer (after this step's operands were read).
+    // During step s: X of step s+1, and -- on the first step of a weight or scale block, or the
+    // range's first step, which can fall inside a block -- the next block into the other buffer
+    // (after this step's operands were read), as long as the range still reaches it.
+    // (The whole-K launch keeps the plain conditions, with kb = 0 and ke = ksteps.)
     auto prefetch_x = [&](int step, unsigned char* xbuf) {
-        if (step + 1 < ksteps) issue_x(step + 1, xbuf);
+        if (step + 1 < (SK ? ke : ksteps)) issue_x(step + 1, xbuf);
     };
     auto prefetch_blocks = [&](int step) {
-        if (step % C::W_SPB == 0 && step / C::W_SPB + 1 < w_blocks)
-            issue_w(step / C::W_SPB + 1, w_buf(step + C::W_SPB));
+        const int wb = step / C::W_SPB;
         const int sb = s_block(step);
-        if ((step == 0 || s_block(step - 1) != sb) && sb + 1 < s_blocks) issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+        if constexpr (SK) {
+            if ((step == kb || step % C::W_SPB == 0) && wb + 1 < w_blocks && (wb + 1) * C::W_SPB < ke)
+                issue_w(wb + 1, ((wb + 1) & 1) ? wk1 : wk0);
+            if ((step == kb || s_block(step - 1) != sb) && sb + 1 < s_blocks && s_block(ke - 1) > sb)
+                issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+        } else {
+            if (step % C::W_SPB == 0 && wb + 1 < w_blocks) issue_w(wb + 1, ((wb + 1) & 1) ? wk1 : wk0);
+            if ((step == 0 || s_block(step - 1) != sb) && sb + 1 < s_blocks) issue_s(sb + 1, ((sb + 1) & 1) ? sk1 : sk0);
+        }
     };
 
-    issue_x(0, xa0);
-    issue_w(0, wk0);
-    issue_s(0, sk0);
+    issue_x(kb, xa0);
+    issue_w(kb / C::W_SPB, w_buf(kb));
+    issue_s(s_block(kb), s_buf(kb));
     wait_vmcnt0();
     __syncthreads();
 
     Ops ops;
-    for (int step = 0; step < ksteps; step += 2) {
+    for (int step = kb; step < ke; step += 2) {
         read_operands(w_buf(step), s_buf(step), step, ops);
         compute(xa0, ops, step, [&]() {
             prefetch_x(step, xa1);
@@ -312,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
         });
         wait_vmcnt0();
         __syncthreads();
-        if (step + 1 >= ksteps) break;
+        if (step + 1 >= ke) break;
         read_operands(w_buf(step + 1), s_buf(step + 1), step + 1, ops);
         compute(xa1, ops, step + 1, [&]() {
             prefetch_x(step + 1, xa0);
@@ -322,18 +345,185 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_tiled_kernel(P
         __syncthreads();
     }
 
-    // ---- epilogue: lane holds column col of each 32x32 block, rows 8*(i/4) + 4*half + i%4 ----
+    if constexpr (!SK) {
+        // ---- epilogue: lane holds column col of each 32x32 block, rows 8*(i/4) + 4*half + i%4 ----
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
+        for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            const int n = n0 + wn0 + nb * 32 + col;
-            if (n >= N) continue;
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int n = n0 + wn0 + nb * 32 + col;
+                if (n >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm0 + mb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                if (m < M) p.Y[int64_t(m) * N + n] = float_to_bf16_bits(acc[mb][nb][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm0 + mb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (m < M) p.Y[int64_t(m) * N + n] = float_to_bf16_bits(acc[mb][nb][i]);
+                }
             }
+        }
+    }
+    };
+
+    // The same epilogue for a stream-K tile (after the range's last segment of it).
+    auto store_y = [&](const GemmProblem& p, int tile) __attribute__((always_inline)) {
+        const int tiles_n = (p.N + BN - 1) / BN;
+        const int m0 = (tile / tiles_n) * BM + wave_m * C::WM, n0 = (tile % tiles_n) * BN + wave_n * C::WN;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int n = n0 + nb * 32 + col;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + mb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (m < p.M) p.Y[int64_t(m) * p.N + n] = float_to_bf16_bits(acc[mb][nb][i]);
+                }
+            }
+        }
+    };
+
+    if constexpr (!SK) {
+        // Workgroup -> (problem, tile); the tiles one XCD runs are contiguous in the group's
+        // tile order.
+        const int t = xcd_remap(blockIdx.x, grp.tile_end[grp.count - 1]);
+        int pi = 0;
+        while (pi + 1 < grp.count && t >= grp.tile_end[pi]) ++pi;
+        const GemmProblem p = grp.p[pi];
+        const int tile = t - (pi > 0 ? grp.tile_end[pi - 1] : 0);
+        run(p, tile, 0, (p.K + KS - 1) / KS);  // the whole K, Y written at its end
+    } else {
+        // The tiles of a workgroup's range run last to first: a tile's first steps are then
+        // the end of one workgroup's range, computed first, and its last steps the start of the
+        // next one's, computed last -- so the workgroup owning a tile's last step is nearly
+        // always the last to finish it, and adds the others' partials to its own registers
+        // without storing them.  Partial tiles travel as 16-byte loads and stores with the sc1
+        // cache policy (through to the device-coherent level: the L2 of one XCD is not
+        // coherent with the others); a workgroup's stores complete before its arrival is
+        // counted.  Every tile's sum runs in one fixed order, last steps first, whichever
+        // workgroup adds it, so results do not depend on timing.  No workgroup waits for
+        // another.
+        const GemmProblem p = grp.p[0];
+        // uniform values in scalar registers (32-bit: the host keeps units * workgroups < 2^31)
+        auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+        const int ksteps = uni((p.K + KS - 1) / KS);
+        const int U = uni(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * ksteps);
+        const int nwg = sk.nwg;
+        const int w = uni(xcd_remap(blockIdx.x, nwg));
+        const int u0 = uni(w * U / nwg), u1 = uni((w + 1) * U / nwg);
+        if (u0 >= u1) return;
+        constexpr int kSc1 = 16;  // cache policy bit sc1 of buffer loads and stores
+        constexpr uint32_t kSlot = uint32_t(BM) * BN * 4u;
+        constexpr int kPairs = C::MB * C::NB * 4;  // (block, quarter) pairs of a lane's accumulators
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc(sk.parts, uint32_t(2 * nwg) * kSlot);
+        __shared__ int sk_last;
+        // A slot holds pair q of wave v's lanes at (q * WAVES + v) KB, lanes contiguous: each wave
+        // moves only its own 1 KB pieces.
+        auto piece = [&](int q) { return (uint32_t(q) * C::WAVES + uint32_t(wave_u)) * 1024u; };
+        // A finisher's staging: two 4 KB buffers per wave in the X tiles, idle between segments.
+        unsigned char* const stg0 = xa0 + wave_u * 4096;
+        unsigned char* const stg1 = xa1 + wave_u * 4096;
+        static_assert(C::X_TILE >= C::WAVES * 4096, "staging does not fit the X tiles");
+        // Y = bf16(acc + the part in slot s), block by block: block b's four 1 KB pieces are
+        // copied into one staging buffer while the previous block is added and stored (direct-
+        // to-LDS copies need no registers while acc holds the tile).
+        auto store_y_plus = [&](int tile, uint32_t s) __attribute__((always_inline)) {
+            const uint32_t base = s * kSlot + uint32_t(lane) * 16u;
+            auto fetch = [&](int b, unsigned char* buf) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) dma16_sc1(prs, buf + i4 * 1024, base + piece(4 * b + i4));
+            };
+            const int tiles_n = (p.N + BN - 1) / BN;
+            const int m0 = (tile / tiles_n) * BM + wave_m * C::WM, n0 = (tile % tiles_n) * BN + wave_n * C::WN;
+            fetch(0, stg0);
+#pragma unroll
+            for (int b = 0; b < C::MB * C::NB; ++b) {
+                if (b + 1 < C::MB * C::NB) {
+                    fetch(b + 1, (b & 1) ? stg0 : stg1);
+                    wait_vmcnt<4>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                const unsigned char* buf = (b & 1) ? stg1 : stg0;
+                const int mb = b / C::NB, nb = b % C::NB;
+                const int n = n0 + nb * 32 + col;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(buf + i4 * 1024 + lane * 16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        const int m = m0 + mb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                        if (n < p.N && m < p.M) p.Y[int64_t(m) * p.N + n] = float_to_bf16_bits(acc[mb][nb][i] + f[e]);
+                    }
+                }
+            }
+        };
+        const int t_first = uni(u0 / ksteps);
+        for (int tile = uni((u1 - 1) / ksteps); tile >= t_first; --tile) {
+            const int tu = tile * ksteps;
+            const int kb = (u0 > tu ? u0 : tu) - tu;
+            const int ke = (u1 < tu + ksteps ? u1 : tu + ksteps) - tu;
+            run(p, tile, kb, ke);
+            if (kb == 0 && ke == ksteps) {
+                store_y(p, tile);
+                continue;
+            }
+            // the tile's workgroups wf .. wl (owners of its first and last unit)
+            const int wf = uni(((tu + 1) * nwg - 1) / U);
+            const int wl = uni(((tu + ksteps) * nwg - 1) / U);
+            uint32_t* counter = sk.counters + wl;
+            // slot of workgroup v's part of this tile: 2v for the tile of v's first unit, else 2v + 1
+            auto slot = [&](int v) { return uint32_t(uni(2 * v + ((v * U / nwg) / ksteps == tile ? 0 : 1))); };
+            if (tid == 0)
+                sk_last = wl - wf == 1 && __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                         uint32_t(wl - wf);
+            __syncthreads();
+            if (!sk_last) {
+                const uint32_t base = slot(w) * kSlot + uint32_t(lane) * 16u;
+#pragma unroll
+                for (int q = 0; q < kPairs; ++q) {
+                    const int bb = q / 4, i4 = q % 4, mb = bb / C::NB, nb = bb % C::NB;
+                    // whole-vector bit cast (a bit cast of one vector element read element 0 here)
+                    const f32x4_t v = {acc[mb][nb][4 * i4], acc[mb][nb][4 * i4 + 1], acc[mb][nb][4 * i4 + 2],
+                                       acc[mb][nb][4 * i4 + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prs, base + piece(q), 0,
+                                                           kSc1);
+                }
+                wait_vmcnt0();
+                __syncthreads();
+                if (tid == 0)
+                    sk_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                              uint32_t(wl - wf);
+                __syncthreads();
+                if (!sk_last) continue;
+            }
+            // Sum = ((P_wl + P_wl-1) + ...) + P_wf.  A two-part tile's finisher owns its last step
+            // (the shortcut above, or the count) and adds the other part to its registers.
+            if (wl - wf == 1) {
+                store_y_plus(tile, slot(w == wl ? wf : wl));
+            } else {
+                // every part is in the workspace: from -0 (-0 + x == x for every x), in the same
+                // order, four outputs at a time
+                const int tiles_n = (p.N + BN - 1) / BN;
+                const int m0 = (tile / tiles_n) * BM + wave_m * C::WM, n0 = (tile % tiles_n) * BN + wave_n * C::WN;
+                for (int q = 0; q < kPairs; ++q) {
+                    f32x4_t t = {-0.0f, -0.0f, -0.0f, -0.0f};
+                    for (int v = wl; v >= wf; --v)
+                        t += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             prs, slot(v) * kSlot + uint32_t(lane) * 16u + piece(q), 0,
+                                                             kSc1));
+                    const int bb = q / 4, i4 = q % 4, mb = bb / C::NB, nb = bb % C::NB;
+                    const int n = n0 + nb * 32 + col;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        const int m = m0 + mb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                        if (n < p.N && m < p.M) p.Y[int64_t(m) * p.N + n] = float_to_bf16_bits(t[e]);
+                    }
+                }
+            }
+            __syncthreads();  // the staging buffers are the next segment's X tiles
+            if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -344,18 +534,45 @@ hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t stream) {
     int total = 0;
     for (int i = 0; i < count; ++i) {
         grp.p[i] = probs[i];
-        total += ((probs[i].M + BM - 1) / BM) * ((probs[i].N + BN - 1) / BN);
+        total += int(tiles_of(probs[i].M, BM) * tiles_of(probs[i].N, BN));
         grp.tile_end[i] = total;
     }
     grp.count = count;
     hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, BM, BN, WAVES_M, WAVES_N, WB>), dim3(total),
-                       dim3(64 * WAVES_M * WAVES_N), 0, stream, grp);
+                       dim3(64 * WAVES_M * WAVES_N), 0, stream, grp, StreamK{});
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess && trace_enabled()) {
         char cfg[64];
         snprintf(cfg, sizeof cfg, "%dx%d waves=%dx%d", BM, BN, WAVES_M, WAVES_N);
         trace_launch("tiled32", cfg, G, BITS, probs, count, unsigned(total), 64u * WAVES_M * WAVES_N, 0u);
     }
+    return e;
+}
+
+// Stream-K on the 256 x 256 tile (8 waves of 128 x 64): one workgroup per compute unit.
+constexpr int kSkBM = 256, kSkBN = 256;
+constexpr size_t kSkCounterBytes = 4096;  // the workspace's counter region (as the resident kernel's)
+
+int streamk_workgroups(const GemmProblem& p) {
+    const int64_t units = tiles_of(p.M, kSkBM) * tiles_of(p.N, kSkBN) * tiles_of(p.K, 64);
+    return int(units < kComputeUnits ? units : kComputeUnits);
+}
+
+template <int BITS, int G>
+hipError_t launch_streamk_cfg(const GemmProblem& p, void* workspace, hipStream_t stream) {
+    ProblemGroup grp{};
+    grp.p[0] = p;
+    grp.count = 1;
+    grp.tile_end[0] = int(tiles_of(p.M, kSkBM) * tiles_of(p.N, kSkBN));
+    StreamK sk{};
+    sk.nwg = streamk_workgroups(p);
+    sk.counters = static_cast<uint32_t*>(workspace);
+    sk.parts = static_cast<unsigned char*>(workspace) + kSkCounterBytes;
+    hipLaunchKernelGGL((gemm_tiled_kernel<BITS, G, kSkBM, kSkBN, 2, 4, 64, true>), dim3(sk.nwg), dim3(512), 0, stream,
+                       grp, sk);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && trace_enabled())
+        trace_launch("tiled32", "256x256 waves=2x4 streamk", G, BITS, &p, 1, unsigned(sk.nwg), 512u, 0u);
     return e;
 }
 
@@ -424,7 +641,7 @@ int pick_tile_variant(const GemmProblem* probs, int count, int g, int bits) {
         }
         int64_t tiles = 0;
         for (int i = 0; i < count; ++i)
-            tiles += int64_t((probs[i].M + t.bm - 1) / t.bm) * ((probs[i].N + t.bn - 1) / t.bn);
+            tiles += tiles_of(probs[i].M, t.bm) * tiles_of(probs[i].N, t.bn);
         const int64_t slots = int64_t(kComputeUnits) * t.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
         if (t.variant == TILE_96x192K2 && rounds > 1) continue;  // single rounds only (see above)
@@ -452,6 +669,7 @@ const char* tile_variant_name(int variant) {
         case TILE_96x192K2: return "tile96x192k2";
         case TILE_64x128K2: return "tile64x128k2";
         case TILE_256x192: return "tile256x192";
+        case TILE_256x256SK: return "tile256x256sk";
         default: return "tile64x256";
     }
 }
@@ -459,6 +677,7 @@ const char* tile_variant_name(int variant) {
 hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, int bits, int variant,
                                    hipStream_t stream) {
     if (bits == 4 && !is_tile16_variant(variant)) variant = TILE_288x192;  // the only 4-bit kernel
+    if (variant == TILE_256x256SK) variant = TILE_256x256;  // stream-K needs a workspace (the grouped launch)
     if (is_tile16_variant(variant)) {
         if (tile16_supported(g, bits)) return launch_gemm_tile16_group(probs, count, g, bits, variant, stream);
         variant = TILE_256x256;
@@ -474,6 +693,33 @@ hipError_t launch_gemm_tiled_group(const GemmProblem* probs, int count, int g, i
         case 32: return launch_bits_g<1, 32>(probs, count, variant, stream);
         case 64: return launch_bits_g<1, 64>(probs, count, variant, stream);
         default: return launch_bits_g<1, 128>(probs, count, variant, stream);
+    }
+}
+
+size_t streamk_workspace_bytes(const GemmProblem& p, int g, int bits) {
+    (void)g;
+    if ((bits != 1 && bits != 2) || p.M <= 0 || p.N <= 0 || p.K <= 0) return 0;
+    // the kernel's partition arithmetic is 32-bit: units x workgroups < 2^31
+    const int64_t units = tiles_of(p.M, kSkBM) * tiles_of(p.N, kSkBN) * tiles_of(p.K, 64);
+    if (units * kComputeUnits >= (int64_t(1) << 31)) return 0;
+    return kSkCounterBytes + 2 * size_t(streamk_workgroups(p)) * size_t(kSkBM) * kSkBN * 4u;
+}
+
+hipError_t launch_gemm_streamk(const GemmProblem& p, int g, int bits, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    const size_t need = streamk_workspace_bytes(p, g, bits);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need) return hipErrorInvalidValue;
+    if (bits == 2) {
+        switch (g) {
+            case 32: return launch_streamk_cfg<2, 32>(p, workspace, stream);
+            case 64: return launch_streamk_cfg<2, 64>(p, workspace, stream);
+            default: return launch_streamk_cfg<2, 128>(p, workspace, stream);
+        }
+    }
+    switch (g) {
+        case 32: return launch_streamk_cfg<1, 32>(p, workspace, stream);
+        case 64: return launch_streamk_cfg<1, 64>(p, workspace, stream);
+        default: return launch_streamk_cfg<1, 128>(p, workspace, stream);
     }
 }
 

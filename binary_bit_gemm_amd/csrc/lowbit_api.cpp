@@ -78,7 +78,8 @@ int device_check() {
 
 // Variant override for A/B runs and tests: LOWBIT_VARIANT = auto | skinny | resident | tile256 | tile256w |
 // tile128 | tile64 | tile288 | tile256n (256 x 192) | tile96 | tile96k2 | tile64k2 (the 16x16-block tiles,
-// tile288 onwards, fall back to tile256w where that kernel does not apply)
+// tile288 onwards, fall back to tile256w where that kernel does not apply) | tile256sk (stream-K on
+// 256 x 256 in the calls that pass a workspace large enough, tile256w in the others)
 int forced_variant() {
     const char* v = std::getenv("LOWBIT_VARIANT");
     if (v == nullptr || std::strcmp(v, "auto") == 0 || v[0] == 0) return -1;
@@ -92,6 +93,7 @@ int forced_variant() {
     if (std::strcmp(v, "tile96k2") == 0) return lowbit::TILE_96x192K2;
     if (std::strcmp(v, "tile256n") == 0) return lowbit::TILE_256x192;
     if (std::strcmp(v, "tile64k2") == 0) return lowbit::TILE_64x128K2;
+    if (std::strcmp(v, "tile256sk") == 0) return lowbit::TILE_256x256SK;
     if (std::strcmp(v, "resident") == 0) return 102;
     return -1;
 }
@@ -280,6 +282,7 @@ const char* lowbit_gemm_variant(int64_t M, int64_t N, int64_t K, int g, int bits
     if (v == 102) return "resident";
     if (bits == 4 && !lowbit::is_tile16_variant(v)) v = lowbit::TILE_288x192;  // as launch_gemm_tiled_group
     if (lowbit::is_tile16_variant(v) && !lowbit::tile16_supported(g, bits)) v = lowbit::TILE_256x256;
+    if (v == lowbit::TILE_256x256SK) v = lowbit::TILE_256x256;  // stream-K runs only with a workspace
     return lowbit::tile_variant_name(v);
 }
 
@@ -440,7 +443,8 @@ int lowbit_gemm_ex(const void* X, const uint32_t* W, const void* S, void* Y, int
     if (st != LOWBIT_OK || M * N == 0) return st;
     if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
     const size_t need = lowbit_workspace_size(M, N, K, g, bits);
-    if (need == 0 || workspace == nullptr || workspace_bytes < need || forced_variant() >= 0)
+    const int f = forced_variant();
+    if (need == 0 || workspace == nullptr || workspace_bytes < need || (f >= 0 && f != lowbit::TILE_256x256SK))
         return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
     st = device_check();
     if (st != LOWBIT_OK) return st;
@@ -455,9 +459,11 @@ int lowbit_gemm_noalloc(const void* X, const uint32_t* W, const void* S, void* Y
                         int g, int bits, void* stream) {
     int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, bits);
     if (st != LOWBIT_OK || M * N == 0) return st;
+    // a forced variant (LOWBIT_VARIANT) runs as lowbit_gemm, whatever workspace it would take
+    if (forced_variant() >= 0) return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
     const size_t need = lowbit_workspace_size(M, N, K, g, bits);
     if (need > LOWBIT_NOALLOC_SCRATCH_BYTES) return LOWBIT_E_SCRATCH;
-    if (need == 0 || forced_variant() >= 0) return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
+    if (need == 0) return lowbit_gemm(X, W, S, Y, M, N, K, g, bits, stream);
     st = device_check();
     if (st != LOWBIT_OK) return st;
     void* ws = nullptr;
@@ -490,7 +496,9 @@ size_t lowbit_batched_workspace_size(const lowbit_problem* problems, int count) 
 int lowbit_gemm_batched_ex(const lowbit_problem* problems, int count, void* workspace, size_t workspace_bytes,
                            void* stream) {
     if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
-    return batched(problems, count, forced_variant() >= 0 ? nullptr : workspace, workspace_bytes, stream);
+    const int f = forced_variant();
+    return batched(problems, count, f >= 0 && f != lowbit::TILE_256x256SK ? nullptr : workspace, workspace_bytes,
+                   stream);
 }
 
 int lowbit_gemm_batched(const lowbit_problem* problems, int count, void* stream) {

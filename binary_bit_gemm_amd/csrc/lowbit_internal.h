@@ -24,6 +24,9 @@ constexpr int kEpiPlain = 0;     // Y = X . W^T
 constexpr int kEpiSwiglu = 1;    // W holds [gate | up] rows: Y = silu(X . Wg^T) * (X . Wu^T)
 constexpr int kEpiResidual = 2;  // Y = R + gate[n] * (X . W^T)
 
+// Tiles of `b` rows or columns over a dimension of n (64-bit: M may be up to 2^31 - 1).
+inline int64_t tiles_of(int64_t n, int64_t b) { return (n + b - 1) / b; }
+
 // Several independent problems of one (g, bits) class in one launch.  Workgroup w of the
 // launch belongs to the first problem i with w < tile_end[i] (inclusive prefix sums of the
 // per-problem workgroup counts) and works on its local tile w - tile_end[i - 1].
@@ -62,12 +65,20 @@ enum TileVariant {
     TILE_256x128 = 0, TILE_256x256 = 1, TILE_128x256 = 2, TILE_64x256 = 3, TILE_288x192 = 4, TILE_96x192 = 5,
     TILE_96x192K2 = 6,  // 96 x 192 with K split between two groups of 4 waves (even step counts)
     TILE_64x128K2 = 7,  // 64 x 128, the same K split (4-bit codes: small output grids)
-    TILE_256x192 = 8    // 256 x 192 in 12 waves of 128 x 32 (M = 4096 in whole rounds at N = 3072)
+    TILE_256x192 = 8,   // 256 x 192 in 12 waves of 128 x 32 (M = 4096 in whole rounds at N = 3072)
+    TILE_256x256SK = 9  // 256 x 256 stream-K through a workspace (TILE_256x256 where none is given)
 };
 inline bool is_tile16_variant(int v) {
     return v == TILE_288x192 || v == TILE_96x192 || v == TILE_96x192K2 || v == TILE_64x128K2 || v == TILE_256x192;
 }
 hipError_t launch_gemm_tiled(const GemmProblem& p, int g, int bits, int variant, hipStream_t stream);
+// Stream-K on the 256 x 256 tile (ternary and binary codes): one workgroup per compute unit,
+// each a contiguous range of the problem's (tile, 64-element step) units; split tiles are summed
+// from fp32 partial tiles in the workspace (its first 4 KiB are arrival counters, zero between
+// calls).  0 bytes: the shape is not covered.
+size_t streamk_workspace_bytes(const GemmProblem& p, int g, int bits);
+hipError_t launch_gemm_streamk(const GemmProblem& p, int g, int bits, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 // Skinny-M kernel (M <= 32): split-K inside a workgroup, fixed-order LDS reduction.
 // Shapes it does not cover (M > 32, K not a whole number of 64-byte row steps, or a

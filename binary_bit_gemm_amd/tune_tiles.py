@@ -36,7 +36,9 @@ TILES = {
     "tile256w": (256, 256, 1), "tile288": (288, 192, 1), "tile256n": (256, 192, 1), "tile128": (128, 256, 2),
     "tile64": (64, 256, 2),
     "tile96": (96, 192, 1), "tile96k2": (96, 192, 1), "tile64k2": (64, 128, 1),
+    "tile256sk": (256, 256, 1),  # stream-K: the work spread evenly over every compute unit
 }
+STREAM_K = {"tile256sk"}
 DEFAULT_SHAPES = [(4608, 3072, 3072), (4608, 9216, 3072), (4608, 18432, 3072), (4608, 3072, 9216),
                   (4608, 3072, 12288), (4096, 4096, 3072), (4096, 3072, 3072), (4096, 9216, 3072),
                   (1536, 3072, 3072), (1536, 9216, 3072)]
@@ -79,7 +81,7 @@ def time_us(fn, reps, warmup):
 def weighted_work(tile, M, N):
     bm, bn, per_cu = TILES[tile]
     tiles = math.ceil(M / bm) * math.ceil(N / bn)
-    rounds = math.ceil(tiles / (CUS * per_cu))
+    rounds = tiles / (CUS * per_cu) if tile in STREAM_K else math.ceil(tiles / (CUS * per_cu))
     return rounds * per_cu * bm * bn
 
 
@@ -103,8 +105,13 @@ def main() -> None:
             os.environ["LOWBIT_VARIANT"] = t
             if t in ("tile96k2", "tile64k2") and (K // 64) % 2:
                 continue
-            us = time_us(lambda: lb.gemm(x, w, s, a.g, a.bits, out=y), a.reps, a.warmup)
+            ws = None
+            if t in STREAM_K:  # partial tiles through a workspace
+                import torch
+                ws = torch.zeros(lb.workspace_size(M, N, K, a.g, a.bits), dtype=torch.uint8, device="cuda")
+            us = time_us(lambda: lb.gemm(x, w, s, a.g, a.bits, out=y, workspace=ws), a.reps, a.warmup)
             row[t] = us
+            del ws
         os.environ.pop("LOWBIT_VARIANT", None)
         base = weighted_work("tile256w", M, N) / row["tile256w"] if "tile256w" in row else None
         for t, us in row.items():

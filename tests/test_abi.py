@@ -258,6 +258,24 @@ def test_gemm_ex_validates_before_the_device():
 SCRATCH = 6
 
 
+def test_streamk_workspace_size(monkeypatch):
+    # stream-K (LOWBIT_VARIANT=tile256sk): the counters plus two 256 KiB partial tiles per workgroup,
+    # one workgroup per compute unit (fewer where the problem has fewer (tile, step) units)
+    sk = 4096 + 2 * 256 * 256 * 256 * 4
+    assert lb.workspace_size(1536, 18432, 3072, 64, 2) == 0      # the automatic choice: no split
+    monkeypatch.setenv("LOWBIT_VARIANT", "tile256sk")
+    assert lb.workspace_size(1536, 18432, 3072, 64, 2) == sk
+    assert lb.workspace_size(4608, 9216, 3072, 128, 1) == sk
+    assert lb.workspace_size(256, 256, 640, 64, 2) == 4096 + 2 * 10 * 256 * 256 * 4   # 10 units
+    assert lb.workspace_size(1536, 18432, 3072, 64, 4) == 0      # 4-bit codes: the 16x16-block tile
+    assert lb.workspace_size(65536, 65536, 4096, 64, 2) > 0      # 2^22 units
+    assert lb.workspace_size(65536, 65536, 8192, 64, 2) == 0     # 2^23 units x 256 workgroups = 2^31
+    L = lb.lib()
+    A = 256
+    # forced variants run as lowbit_gemm in the allocation-free entry point: no scratch error
+    assert L.lowbit_gemm_noalloc(A, A, A, A + 8, 1536, 18432, 3072, 64, 2, None) == ALIGN
+
+
 def test_noalloc_validates_before_the_device(monkeypatch):
     L = lb.lib()
     A = 256

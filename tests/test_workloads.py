@@ -62,6 +62,8 @@ def test_bench_reads_kernel_variants_from_the_launch_log():
             "tile256x192",
         "lowbit: tiled32 256x256 waves=2x4 g=128 bits=1 grid=216 block=512 lds=0 problems=4608x3072x3072":
             "tile256x256",
+        "lowbit: tiled32 256x256 waves=2x4 streamk g=128 bits=1 grid=256 block=512 lds=0 problems=4608x9216x3072":
+            "tile256x256sk",
         "lowbit: resident column_blocks=7 k_slices=2 steps=6 splits=1 tiles=247 epi=plain g=64 bits=2 grid=247 "
         "block=896 lds=110000 problems=16x27648x3072": "resident",
         "lowbit: skinny row_blocks=1 column_blocks=1 waves=4 g=64 bits=2 grid=384 block=256 lds=0 "
