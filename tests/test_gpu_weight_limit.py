@@ -1,12 +1,14 @@
-"""GPU parity at the size limits.  Packed weights at the header's limit (N * K * bits / 8 <= 2^32 - 1 bytes): K = 2^16
-with N = 2^18 - 16 ternary rows (4 GiB - 256 KiB of packed words) or 2^19 - 16 binary rows, on the
-skinny kernel and the three tile kernels.  Every weight and scale read goes through a buffer
-resource whose 32-bit range covers the whole matrix, and each row's offset is a 32-bit product; the
-columns checked against the oracle include the rows on both sides of the 2 GiB offset and the last.
+"""GPU parity at the size limits.
 
-The packed words and scales are drawn on the device (random words whose ternary fields are made
-valid: 11 becomes 01); the oracle gets the checked rows of those inputs, unpacked by its own
-unpack.  Activations past 4 GiB (2^20 + 40 rows of 4096): every row offset past 2^32 bytes."""
+Packed weights at the header's limit (N * K * bits / 8 <= 2^32 - 1 bytes): K = 2^16 with
+N = 2^18 - 16 ternary rows (4 GiB - 256 KiB of packed words) or 2^19 - 16 binary rows, on the skinny
+kernel and the three tile kernels.  Every weight and scale read goes through a buffer resource whose
+32-bit range covers the whole matrix, and each row's offset is a 32-bit product; the rows checked
+against the oracle include both sides of the 2 GiB offset and the last.  The packed words and
+scales are drawn on the device (random words whose ternary fields are made valid: 11 becomes 01);
+the oracle gets the checked rows of those inputs, unpacked by its own unpack.
+
+Activations past 4 GiB (2^20 + 40 rows of 4096): row offsets pass 2^31 and 2^32 bytes."""
 from __future__ import annotations
 
 import numpy as np
