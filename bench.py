@@ -140,6 +140,9 @@ def parse():
                              "swiglu16", "residual", "te4", "te4_sym"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ramp-ms", type=float, default=50.0,
+                    help="untimed run of the step before the warm-up steps, so that the timed steps "
+                         "find the GPU at its sustained clock (0: none)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of X in the CPU oracle sample (0 = all rows of the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -372,10 +375,7 @@ def main():
         for grp in groups:
             launch(grp)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    variants = launched_variants(step)  # one more warm-up step, with the launch log on
+    variants = launched_variants(step)  # one untimed step with the launch log on
 
     # optionally the step as one HIP graph (captured on a side stream, replayed on the current one)
     graph = None
@@ -392,6 +392,19 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
     run_step = graph.replay if graph is not None else step
+
+    # Clock ramp, then the W warm-up steps, back to back: under continuous load the GPU's clock
+    # rises over the first ~15 ms (per-step HIP events of res1024: 1.43 ms per step at first,
+    # 1.31 ms from about the twelfth step on), so a short warm-up leaves the first timed steps
+    # on a rising clock.  The step runs for about --ramp-ms first (a step count from one timed
+    # step), and only the synchronisation of the timed region separates the warm-up from it.
+    r0 = time.perf_counter()
+    run_step()
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - r0) * 1e3
+    ramp_steps = int(a.ramp_ms / max(one_ms, 1e-3)) + 1 if a.ramp_ms > 0 else 0
+    for _ in range(ramp_steps + a.warmup):
+        run_step()
 
     # timed region: exactly `steps` steps between two synchronisations, bracketed by HIP
     # events on the stream the launches go to
@@ -453,7 +466,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "gemms_per_step": len(probs), "launches_per_step": launches,
                    "workspace_bytes": need,
-                   "graph": graph is not None,
+                   "graph": graph is not None, "clock_ramp_steps": ramp_steps,
                    "shapes": sorted({f"{p.M}x{p.N}x{p.K}" for p in probs}),
                    "bits": sorted({p.bits for p in probs}), "g": sorted({p.g for p in probs}),
                    "flop_per_step": flops_step, "bytes_per_step": bytes_step,
