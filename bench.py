@@ -398,11 +398,12 @@ def main():
     # 1.31 ms from about the twelfth step on), so a short warm-up leaves the first timed steps
     # on a rising clock.  The step runs for about --ramp-ms first (a step count from one timed
     # step), and only the synchronisation of the timed region separates the warm-up from it.
-    r0 = time.perf_counter()
-    run_step()
-    torch.cuda.synchronize()
-    one_ms = (time.perf_counter() - r0) * 1e3
-    ramp_steps = int(a.ramp_ms / max(one_ms, 1e-3)) + 1 if a.ramp_ms > 0 else 0
+    ramp_steps = 0
+    if a.ramp_ms > 0:
+        r0 = time.perf_counter()
+        run_step()
+        torch.cuda.synchronize()
+        ramp_steps = int(a.ramp_ms / max((time.perf_counter() - r0) * 1e3, 1e-3)) + 1
     for _ in range(ramp_steps + a.warmup):
         run_step()
 
