@@ -348,7 +348,10 @@ def main():
     # counters at zero) for the calls that split K across workgroups
     need = 0
     for grp in groups:
-        if len(grp) == 1:
+        if len(grp) == 1 and grp[0] in biases:
+            p = probs[grp[0]]
+            need = max(need, lb.affine_workspace_size(p.M, p.N, p.K, p.g))
+        elif len(grp) == 1:
             p = probs[grp[0]]
             need = max(need, lb.workspace_size(p.M, p.N, p.K, p.g, p.bits))
         else:
@@ -364,7 +367,7 @@ def main():
             lb.gemm_residual(x, w, s, g, bits, res_r, res_g, out=y)
         elif len(grp) == 1 and grp[0] in biases:
             x, w, s, y, g, bits = bufs[grp[0]]
-            lb.gemm_affine(x, w, s, biases[grp[0]], g, out=y)
+            lb.gemm_affine(x, w, s, biases[grp[0]], g, out=y, workspace=ws)
         elif len(grp) == 1:
             x, w, s, y, g, bits = bufs[grp[0]]
             lb.gemm(x, w, s, g, bits, out=y, workspace=ws)

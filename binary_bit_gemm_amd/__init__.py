@@ -90,9 +90,16 @@ def pack_u4(levels, count_invalid: bool = True):
     return words, (int(bad.item()) if bad is not None else None)
 
 
-def gemm_affine(x, words, scales, biases, g: int, out=None):
+def affine_workspace_size(M: int, N: int, K: int, g: int = 64) -> int:
+    """Bytes of workspace lowbit_gemm_affine_ex can use for this shape (0: it takes no split)."""
+    return int(lib().lowbit_affine_workspace_size(M, N, K, g))
+
+
+def gemm_affine(x, words, scales, biases, g: int, out=None, workspace=None):
     """Y = X . W^T with affine 4-bit groups W = S * q + B (lowbit_gemm_affine): `words` from
-    pack_u4, `scales` and `biases` fp16 [N, K/g]."""
+    pack_u4, `scales` and `biases` fp16 [N, K/g].  `workspace`: an optional zero-filled device
+    tensor of at least affine_workspace_size(M, N, K, g) bytes (lowbit_gemm_affine_ex), with which
+    shapes whose tile grid leaves compute units idle split K across workgroups."""
     torch = _torch()
     _require(x, torch.bfloat16, "x")
     _require(words, torch.int32, "words")
@@ -110,10 +117,18 @@ def gemm_affine(x, words, scales, biases, g: int, out=None):
         _require(out, torch.bfloat16, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [M, N]")
-    st = lib().lowbit_gemm_affine(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()),
-                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(biases.data_ptr()),
-                                  ctypes.c_void_p(out.data_ptr()), M, N, K, g, ctypes.c_void_p(_stream_ptr(x.device)))
-    _check(st, "lowbit_gemm_affine")
+    args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(words.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+            ctypes.c_void_p(biases.data_ptr()), ctypes.c_void_p(out.data_ptr()), M, N, K, g)
+    if workspace is None:
+        st = lib().lowbit_gemm_affine(*args, ctypes.c_void_p(_stream_ptr(x.device)))
+        _check(st, "lowbit_gemm_affine")
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        st = lib().lowbit_gemm_affine_ex(*args, ctypes.c_void_p(workspace.data_ptr()), nbytes,
+                                         ctypes.c_void_p(_stream_ptr(x.device)))
+        _check(st, "lowbit_gemm_affine_ex")
     return out
 
 

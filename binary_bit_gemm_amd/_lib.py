@@ -15,6 +15,8 @@ SIGNATURES = {
     "lowbit_unpack": (_INT, [_VP, _VP, _I64, _I64, _INT, _VP]),
     "lowbit_pack_u4": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP]),
     "lowbit_gemm_affine": (_INT, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
+    "lowbit_affine_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _INT]),
+    "lowbit_gemm_affine_ex": (_INT, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP, ctypes.c_size_t, _VP]),
     "lowbit_import_ternary": (_INT, [_VP, _INT, _INT, _VP, _I64, _I64, _VP, _VP]),
     "lowbit_import_binary_gemlite": (_INT, [_VP, _VP, _I64, _I64, _VP]),
     "lowbit_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),

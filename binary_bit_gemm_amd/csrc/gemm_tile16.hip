@@ -87,9 +87,20 @@ struct Cfg16 {
 // b * (sum of the group's activations); that row sum comes from one MFMA pair against an all-ones
 // operand per row block (exact products, fp32 sums, in the accumulator layout), shared by the
 // wave's column blocks, and enters with one more fp32 FMA per output and group.
+// XSPLIT: K split across `sk.splits` workgroups per tile (workgroup b runs split b / tiles of tile
+// b % tiles), for grids that leave compute units idle.  Each split's workgroup stores its fp32 sums
+// in the caller's workspace and counts itself in on the tile's counter; the last to arrive adds the
+// splits' sums in split order 0, 1, ... (a fixed order: the result does not depend on timing),
+// resets the counter and runs the epilogue.
+struct SplitK {
+    float* ws;            // [tiles][splits][waves][MB * NB][64 lanes][4] fp32 sums
+    uint32_t* counters;   // [tiles], zero between calls
+    int splits;
+};
+
 template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT, int EPI = kEpiPlain,
-          bool AFFINE = false>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp) {
+          bool AFFINE = false, bool XSPLIT = false>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile16_kernel(ProblemGroup grp, SplitK sk) {
     constexpr bool SWIGLU = EPI == kEpiSwiglu;
     static_assert(!AFFINE || (BITS == 4 && EPI == kEpiPlain), "affine groups: 4-bit levels, plain epilogue");
     using C = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
@@ -156,8 +167,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
         // the group's steps [kbeg, kend); every group has the same count (the host sends
         // KSPLIT = 2 only for an even step count), so all run the same barriers
         const int ksteps = c.K / KS;
-        c.kbeg = kg * (ksteps / KSPLIT);
-        c.kend = c.kbeg + ksteps / KSPLIT;
+        if constexpr (XSPLIT) {
+            const int sp = int(blockIdx.x) / total_tiles;
+            c.kbeg = sp * ksteps / sk.splits;
+            c.kend = (sp + 1) * ksteps / sk.splits;
+        } else {
+            c.kbeg = kg * (ksteps / KSPLIT);
+            c.kend = c.kbeg + ksteps / KSPLIT;
+        }
         c.w_row_bytes = uint32_t(c.K) * BITS / 8u;
         c.s_row_bytes = uint32_t(c.K / G) * 2u;
         c.x_voff = uint32_t(r_first) * uint32_t(c.K) * 2u + uint32_t((tid % kXChunks) ^ lds_swizzle(r_first)) * 16u;
@@ -238,9 +255,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
     // (grid below the tile count, a multiple of the 8 XCDs, so that every virtual id keeps its
     // workgroup's XCD and xcd_remap's tile order) saves the next workgroup's launch on the
     // compute unit, and the next tile's first copies go out before this tile's epilogue.
-    TileCtx cur = tile_ctx(int(blockIdx.x));
+    static_assert(!XSPLIT || (KSPLIT == 1 && !SWIGLU), "K split across workgroups: one K group, plain epilogue");
+    int vt = XSPLIT ? int(blockIdx.x) % total_tiles : int(blockIdx.x);
+    TileCtx cur = tile_ctx(vt);
     issue_first(cur);
-    int vt = int(blockIdx.x);
 #pragma nounroll
     for (;;) {
         const GemmProblem p = cur.p;
@@ -516,12 +534,65 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 
         // ---- the next tile's first copies, once every wave is done with this tile's buffers ----
         const int vn = vt + int(gridDim.x);
-        const bool more = KSPLIT == 1 && vn < total_tiles;
+        const bool more = KSPLIT == 1 && !XSPLIT && vn < total_tiles;
         TileCtx nxt;
         if (more) {
             nxt = tile_ctx(vn);
             __syncthreads();
             issue_first(nxt);
+        }
+
+        // ---- K split across workgroups: this split's sums to the workspace, the last one adds ----
+        // (16-byte loads and stores with the sc1 cache policy: through to the device-coherent
+        // level, since the L2 of one XCD is not coherent with the others; the stores complete
+        // before the arrival is counted)
+        if constexpr (XSPLIT) {
+            constexpr int kSc1 = 16;
+            constexpr int kBlocks = C::MB * C::NB;
+            const int t = xcd_remap(vt, total_tiles);
+            const int sp = int(blockIdx.x) / total_tiles;
+            const uint32_t wave_bytes = uint32_t(kBlocks) * 1024u;
+            const uint32_t tile_bytes = uint32_t(sk.splits) * uint32_t(C::WAVES) * wave_bytes;
+            const __amdgpu_buffer_rsrc_t ws_rs = make_rsrc(sk.ws, uint32_t(total_tiles) * tile_bytes);
+            const uint32_t mine = uint32_t(t) * tile_bytes + (uint32_t(sp) * uint32_t(C::WAVES) + uint32_t(wave)) * wave_bytes +
+                                  16u * uint32_t(lane);
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mb][nb]), ws_rs,
+                                                           mine + uint32_t(mb * C::NB + nb) * 1024u, 0, kSc1);
+            wait_vmcnt0();
+            __syncthreads();
+            __shared__ int last_split;
+            if (threadIdx.x == 0)
+                last_split = __hip_atomic_fetch_add(&sk.counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                             uint32_t(sk.splits - 1);
+            __syncthreads();
+            if (!last_split) return;
+            // every split's sums, split by split, added in split order
+            const uint32_t first = uint32_t(t) * tile_bytes + uint32_t(wave) * wave_bytes + 16u * uint32_t(lane);
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int s2 = 0; s2 < sk.splits; ++s2) {
+                u32x4_t part[kBlocks];
+                const uint32_t src = first + uint32_t(s2) * uint32_t(C::WAVES) * wave_bytes;
+#pragma unroll
+                for (int b = 0; b < kBlocks; ++b)
+                    part[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ws_rs, src + uint32_t(b) * 1024u,
+                                                                                              0, kSc1));
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; ++nb) {
+                        const f32x4_t f = __builtin_bit_cast(f32x4_t, part[mb * C::NB + nb]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mb][nb][i] += f[i];
+                    }
+            }
+            if (threadIdx.x == 0) __hip_atomic_store(&sk.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
         // ---- epilogue ----
@@ -596,8 +667,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * KSPLIT, 1) void gemm_tile1
 }
 
 template <int G, int BITS, int BM, int BN, int WAVES_M, int WAVES_N, int KSPLIT = 1, int EPI = kEpiPlain,
-          bool AFFINE = false>
-hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream) {
+          bool AFFINE = false, bool XSPLIT = false>
+hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream, SplitK sk = SplitK{}) {
     ProblemGroup grp{};
     int total = 0;
     constexpr int kOutBn = EPI == kEpiSwiglu ? BN / 2 : BN;
@@ -612,14 +683,15 @@ hipError_t launch_cfg16(const GemmProblem* probs, int count, hipStream_t stream)
     using Cf = Cfg16<G, BITS, BM, BN, WAVES_M, WAVES_N>;
     constexpr int kLds = KSPLIT * 2 * (Cf::X_TILE + Cf::W_BLOCK + Cf::S_BLOCK + (AFFINE ? Cf::S_BLOCK : 16));
     constexpr bool kPersistent = KSPLIT == 1 && kLds > 80 * 1024;
-    const int grid = kPersistent && total > kComputeUnits ? kComputeUnits : total;
-    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI, AFFINE>), dim3(grid),
-                       dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp);
+    const int grid = XSPLIT ? total * sk.splits : kPersistent && total > kComputeUnits ? kComputeUnits : total;
+    hipLaunchKernelGGL((gemm_tile16_kernel<G, BITS, BM, BN, WAVES_M, WAVES_N, KSPLIT, EPI, AFFINE, XSPLIT>), dim3(grid),
+                       dim3(64 * WAVES_M * WAVES_N * KSPLIT), 0, stream, grp, sk);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess && trace_enabled()) {
         char cfg[96];
-        snprintf(cfg, sizeof cfg, "%dx%d waves=%dx%dx%d epi=%s%s", BM, BN, WAVES_M, WAVES_N, KSPLIT,
-                 EPI == kEpiSwiglu ? "swiglu" : EPI == kEpiResidual ? "residual" : "plain", AFFINE ? " affine" : "");
+        snprintf(cfg, sizeof cfg, "%dx%d waves=%dx%dx%d epi=%s%s splits=%d", BM, BN, WAVES_M, WAVES_N, KSPLIT,
+                 EPI == kEpiSwiglu ? "swiglu" : EPI == kEpiResidual ? "residual" : "plain", AFFINE ? " affine" : "",
+                 XSPLIT ? sk.splits : 1);
         trace_launch("tile16", cfg, G, BITS, probs, count, unsigned(grid), 64u * WAVES_M * WAVES_N * KSPLIT, 0u);
     }
     return e;
@@ -678,6 +750,32 @@ hipError_t launch_gemm_tile16_epilogue(const GemmProblem* probs, int count, int 
     if (epi == kEpiSwiglu) return launch_epi16_gb<kEpiSwiglu>(probs, count, g, bits, stream);
     if (epi == kEpiResidual) return launch_epi16_gb<kEpiResidual>(probs, count, g, bits, stream);
     return hipErrorInvalidValue;
+}
+
+// Affine 4-bit GEMMs whose 64 x 128 tile grid leaves a quarter of the compute units or more idle
+// (the text encoder's 512 x 2560 down projection: 160 tiles) split K three ways across workgroups
+// through a caller workspace: three 4-wave workgroups of 48 KB LDS share a compute unit, so the
+// 480 workgroups run in one round.  0 where no split applies.
+constexpr int kAffineSplits = 3;
+constexpr size_t kAffineCounterBytes = 4096;  // 1024 tile counters, at the workspace's start
+size_t affine_split_bytes(const GemmProblem& p, int g) {
+    if (!tile16_supported(g, 4) || pick_tile_variant(&p, 1, g, 4) != TILE_64x128K2) return 0;
+    const int64_t tiles = tiles_of(p.M, 64) * tiles_of(p.N, 128);
+    if (tiles * 4 > int64_t(kComputeUnits) * 3 || tiles > 1024 || p.K / KS < 8 * kAffineSplits) return 0;
+    using Cf = Cfg16<64, 4, 64, 128, 1, 4>;
+    return kAffineCounterBytes + size_t(tiles) * kAffineSplits * Cf::WAVES * Cf::MB * Cf::NB * 1024u;
+}
+
+size_t affine_workspace_bytes(const GemmProblem& p, int g) { return affine_split_bytes(p, g); }
+
+hipError_t launch_gemm_tile16_affine_ex(const GemmProblem& p, int g, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    const size_t need = affine_split_bytes(p, g);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need) return hipErrorNotSupported;
+    SplitK sk{reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kAffineCounterBytes),
+              static_cast<uint32_t*>(workspace), kAffineSplits};
+    return g == 64 ? launch_cfg16<64, 4, 64, 128, 1, 4, 1, kEpiPlain, true, true>(&p, 1, stream, sk)
+                   : launch_cfg16<128, 4, 64, 128, 1, 4, 1, kEpiPlain, true, true>(&p, 1, stream, sk);
 }
 
 hipError_t launch_gemm_tile16_affine(const GemmProblem* probs, int count, int g, int variant, hipStream_t stream) {

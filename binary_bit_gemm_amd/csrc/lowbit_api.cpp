@@ -305,6 +305,36 @@ int lowbit_pack_u4(const uint8_t* levels, uint32_t* W, int64_t N, int64_t K, int
     return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
 }
 
+size_t lowbit_affine_workspace_size(int64_t M, int64_t N, int64_t K, int g) {
+    if (lowbit_check_gemm_args(reinterpret_cast<const void*>(256), reinterpret_cast<const uint32_t*>(256),
+                               reinterpret_cast<const void*>(256), reinterpret_cast<const void*>(256), M, N, K, g,
+                               4) != LOWBIT_OK ||
+        M * N * K == 0)
+        return 0;
+    const lowbit::GemmProblem p{nullptr, nullptr, nullptr, nullptr, int(M), int(N), int(K)};
+    return lowbit::affine_workspace_bytes(p, g);
+}
+
+int lowbit_gemm_affine_ex(const void* X, const uint32_t* W, const void* S, const void* B, void* Y, int64_t M,
+                          int64_t N, int64_t K, int g, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, 4);
+    if (st != LOWBIT_OK || M * N == 0) return st;
+    if (K > 0 && B == nullptr) return LOWBIT_E_INVALID;
+    if (K > 0 && !aligned16(B)) return LOWBIT_E_ALIGN;
+    if (workspace != nullptr && !aligned16(workspace)) return LOWBIT_E_ALIGN;
+    const size_t need = lowbit_affine_workspace_size(M, N, K, g);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need || forced_variant() >= 0)
+        return lowbit_gemm_affine(X, W, S, B, Y, M, N, K, g, stream);
+    st = device_check();
+    if (st != LOWBIT_OK) return st;
+    lowbit::GemmProblem p{static_cast<const uint16_t*>(X), W, static_cast<const uint16_t*>(S),
+                          static_cast<uint16_t*>(Y), int(M), int(N), int(K)};
+    p.B = static_cast<const uint16_t*>(B);
+    const hipError_t e = lowbit::launch_gemm_tile16_affine_ex(p, g, workspace, workspace_bytes,
+                                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWBIT_OK : hip_fail(e);
+}
+
 int lowbit_gemm_affine(const void* X, const uint32_t* W, const void* S, const void* B, void* Y, int64_t M,
                        int64_t N, int64_t K, int g, void* stream) {
     int st = lowbit_check_gemm_args(X, W, S, Y, M, N, K, g, 4);

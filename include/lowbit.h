@@ -290,6 +290,26 @@ int lowbit_gemm_residual(const void* X, const uint32_t* W, const void* S, const 
 int lowbit_gemm_affine(const void* X, const uint32_t* W, const void* S, const void* B, void* Y,
                        int64_t M, int64_t N, int64_t K, int g, void* stream);
 
+/*
+ * lowbit_affine_workspace_size / lowbit_gemm_affine_ex -- lowbit_gemm_affine with a caller-provided
+ * workspace, with which the call splits K across workgroups where the output tile grid leaves a
+ * quarter of the compute units or more idle (the text encoder's 512 x 2560 down projection at
+ * K = 9728, a shape of the mlx guide's component architecture): three workgroups per output tile,
+ * whose fp32 sums are added in a fixed split order (deterministic; the last bits can differ from
+ * lowbit_gemm_affine's, which runs K in one workgroup).
+ *   workspace        device memory of at least lowbit_affine_workspace_size(...) bytes, 16-byte
+ *                    aligned, ZERO-FILLED before its first use; its first 4096 bytes hold arrival
+ *                    counters that every call leaves at zero again, so one workspace serves calls
+ *                    of any shapes in turn.  Calls that share a workspace must not run concurrently.
+ *   workspace_bytes  its size.  With a NULL or too small workspace, or for shapes that take no
+ *                    split (size 0), the call is exactly lowbit_gemm_affine.
+ * lowbit_affine_workspace_size returns 0 for invalid arguments and for shapes that take no split.
+ */
+size_t lowbit_affine_workspace_size(int64_t M, int64_t N, int64_t K, int g);
+int lowbit_gemm_affine_ex(const void* X, const uint32_t* W, const void* S, const void* B, void* Y,
+                          int64_t M, int64_t N, int64_t K, int g, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Host-only argument check of lowbit_gemm (no HIP call): returns the status lowbit_gemm
  * would return before touching the device. */
 int lowbit_check_gemm_args(const void* X, const uint32_t* W, const void* S, const void* Y,

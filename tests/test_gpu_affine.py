@@ -196,3 +196,37 @@ def test_edge_cases():
     # the empty pack
     w0, bad = lb.pack_u4(t.zeros((0, 64), dtype=t.uint8, device="cuda"))
     assert bad == 0 and tuple(w0.shape) == (0, 8)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(512, 2560, 9728, 64), (64, 1024, 1536, 64), (100, 1040, 3072, 128),
+                                     (37, 400, 2944, 64)])
+def test_split_k_through_workspace(M, N, K, g):
+    """lowbit_gemm_affine_ex: K split across three workgroups per tile where the 64 x 128 grid leaves
+    compute units idle (the text encoder's down projection, smaller grids, ragged M and N, uneven
+    K ranges), against the oracle; bitwise the same on a second call with the same workspace, whose
+    arrival counters are back at zero after each call."""
+    t = torch()
+    need = lb.affine_workspace_size(M, N, K, g)
+    assert need > 4096, (M, N, K, g, need)
+    inp = W.make_inputs(_problem(M, N, K, g, cid=129), seed=9)
+    words, _ = lb.pack_u4(_dev_levels(inp.codes))
+    x, s, b = dev_x(inp.x), dev_scales(inp.scales), dev_scales(inp.biases)
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    y1 = host_bits(lb.gemm_affine(x, words, s, b, g, workspace=ws))
+    assert not ws[:4096].any().item(), "arrival counters not reset"
+    y2 = host_bits(lb.gemm_affine(x, words, s, b, g, workspace=ws))
+    assert np.array_equal(y1, y2), "split-K result not deterministic"
+    rows = None if M <= 128 else np.array(sorted(set(range(24)) | set(range(M - 24, M)) | {63, 64, 127, 128, 255, 256}))
+    _check(y1, inp, g, f"split K {M}x{N}x{K} g{g}", rows=rows)
+    # too small a workspace: exactly the unsplit call
+    small = t.zeros(need - 16, dtype=t.uint8, device="cuda")
+    y0 = host_bits(lb.gemm_affine(x, words, s, b, g))
+    assert np.array_equal(host_bits(lb.gemm_affine(x, words, s, b, g, workspace=small)), y0)
+
+
+def test_split_k_sizes():
+    # shapes whose grid fills the machine, or with too few steps, take no split
+    assert lb.affine_workspace_size(512, 19456, 2560, 64) == 0
+    assert lb.affine_workspace_size(4096, 2560, 9728, 64) == 0
+    assert lb.affine_workspace_size(64, 1024, 1024, 64) == 0
+    assert lb.affine_workspace_size(512, 2560, 9728, 32) == 0
