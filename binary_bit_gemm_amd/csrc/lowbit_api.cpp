@@ -15,6 +15,13 @@
 
 namespace lowbit {
 
+// The affine GEMM with K split across workgroups through a caller workspace (gemm_tile16.hip;
+// hipErrorNotSupported where the shape takes no split or the workspace is too small), and the
+// workspace it needs.
+hipError_t launch_gemm_tile16_affine_ex(const GemmProblem& p, int g, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+size_t affine_workspace_bytes(const GemmProblem& p, int g);
+
 bool trace_enabled() {
     const char* v = std::getenv("LOWBIT_TRACE");
     return v != nullptr && v[0] != 0 && std::strcmp(v, "0") != 0;

@@ -131,11 +131,6 @@ hipError_t launch_gemm_tile16_group(const GemmProblem* probs, int count, int g, 
 // Affine 4-bit groups (unsigned levels, w = s * q + b with each problem's B set) on a 16x16-block
 // tile; `variant` as for 4-bit codes.
 hipError_t launch_gemm_tile16_affine(const GemmProblem* probs, int count, int g, int variant, hipStream_t stream);
-// The affine GEMM with K split across workgroups through a caller workspace (hipErrorNotSupported
-// where the shape takes no split or the workspace is too small), and the workspace it needs.
-hipError_t launch_gemm_tile16_affine_ex(const GemmProblem& p, int g, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream);
-size_t affine_workspace_bytes(const GemmProblem& p, int g);
 bool use_skinny(int64_t M, int64_t N, int64_t K, int g, int bits);
 
 }  // namespace lowbit
